@@ -1,0 +1,182 @@
+"""CPU oracle for MoE dispatch/combine (test infrastructure).
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  It wraps ``moe_oracle.c`` (plain C,
+single-threaded) with ctypes over NumPy arrays and shares nothing with the HIP
+library in ``combine_group_limited_amd``.
+
+Which passage each function follows is stated in ``moe_oracle.c``:
+route -- Perplexity "Efficient and Portable Mixture-of-Experts Communication",
+section "Introduction", and the GeekNews DeepEP digest (group-limited gating);
+layout/dispatch -- same Perplexity page, sections "Portable kernels" and
+"Dispatch"; combine -- section "Combine".
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "moe_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+CFLAGS = ["-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared"]
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (no contraction, no fast-math)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", *CFLAGS, "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build()
+        L = ctypes.CDLL(_LIB)
+        P = ctypes.c_void_p
+        i32, i64 = ctypes.c_int, ctypes.c_int64
+        L.orc_exp_r.restype = ctypes.c_float
+        L.orc_exp_r.argtypes = [ctypes.c_float]
+        L.orc_sigmoid.restype = ctypes.c_float
+        L.orc_sigmoid.argtypes = [ctypes.c_float]
+        for name in ("orc_exp_r_array", "orc_sigmoid_array", "orc_e4m3_from_f32_array",
+                     "orc_bf16_from_f64_array"):
+            getattr(L, name).restype = None
+            getattr(L, name).argtypes = [P, P, i64]
+        L.orc_e4m3_value.restype = ctypes.c_double
+        L.orc_e4m3_value.argtypes = [ctypes.c_uint8]
+        L.orc_route.restype = i32
+        L.orc_route.argtypes = [i32] * 8 + [P, P, P]
+        L.orc_layout.restype = i32
+        L.orc_layout.argtypes = [i32] * 5 + [P] * 8
+        L.orc_dispatch.restype = i32
+        L.orc_dispatch.argtypes = [i32] * 5 + [P] * 4
+        L.orc_combine.restype = i32
+        L.orc_combine.argtypes = [i32] * 4 + [P] * 4
+        _lib = L
+    return _lib
+
+
+def _p(a: np.ndarray):
+    assert a.flags["C_CONTIGUOUS"]
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def exp_r(z) -> np.ndarray:
+    z = np.ascontiguousarray(z, dtype=np.float32)
+    out = np.empty_like(z)
+    lib().orc_exp_r_array(_p(z), _p(out), z.size)
+    return out
+
+
+def sigmoid(x) -> np.ndarray:
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.empty_like(x)
+    lib().orc_sigmoid_array(_p(x), _p(out), x.size)
+    return out
+
+
+def e4m3_value(code: int) -> float:
+    return lib().orc_e4m3_value(code)
+
+
+def e4m3_from_f32(y) -> np.ndarray:
+    y = np.ascontiguousarray(y, dtype=np.float32)
+    out = np.empty(y.shape, dtype=np.uint8)
+    lib().orc_e4m3_from_f32_array(_p(y), _p(out), y.size)
+    return out
+
+
+def bf16_from_f64(v) -> np.ndarray:
+    v = np.ascontiguousarray(v, dtype=np.float64)
+    out = np.empty(v.shape, dtype=np.uint16)
+    lib().orc_bf16_from_f64_array(_p(v), _p(out), v.size)
+    return out
+
+
+SIGMOID, SOFTMAX = 0, 1
+
+
+def route(logits: np.ndarray, num_groups: int, topk_group: int, topk: int,
+          score_fn: int = SIGMOID, renormalize: bool = True, group_topn: int = 0):
+    """Returns (idx int32 [T,k], w float32 [T,k])."""
+    logits = np.ascontiguousarray(logits, dtype=np.float32)
+    T, E = logits.shape
+    idx = np.empty((T, topk), dtype=np.int32)
+    w = np.empty((T, topk), dtype=np.float32)
+    rc = lib().orc_route(T, E, num_groups, topk_group, topk, group_topn, score_fn,
+                         int(renormalize), _p(logits), _p(idx), _p(w))
+    if rc != 0:
+        raise ValueError("oracle route: invalid arguments")
+    return idx, w
+
+
+def layout(idx: np.ndarray, num_experts: int, num_ranks: int, capacity: int = 0):
+    """Returns a dict with cnt_e, cnt_r, off_e, off_r, pos, recv_src, flags."""
+    idx = np.ascontiguousarray(idx, dtype=np.int32)
+    T, k = idx.shape
+    E, R = num_experts, num_ranks
+    N = E * capacity if capacity > 0 else T * k
+    out = dict(
+        cnt_e=np.zeros(E, np.int32), cnt_r=np.zeros(R, np.int32),
+        off_e=np.zeros(E + 1, np.int32), off_r=np.zeros(R + 1, np.int32),
+        pos=np.zeros((T, k), np.int32), recv_src=np.zeros(N, np.int32),
+        flags=np.zeros(1, np.int32),
+    )
+    rc = lib().orc_layout(T, E, k, R, capacity, _p(idx), _p(out["cnt_e"]), _p(out["cnt_r"]),
+                          _p(out["off_e"]), _p(out["off_r"]), _p(out["pos"]),
+                          _p(out["recv_src"]), _p(out["flags"]))
+    if rc != 0:
+        raise ValueError("oracle layout: invalid arguments")
+    out["flags"] = int(out["flags"][0])
+    return out
+
+
+FP8, BF16 = 0, 1
+
+
+def dispatch(x_bits: np.ndarray, pos: np.ndarray, num_recv_rows: int, dtype: int = FP8,
+             recv_x: np.ndarray | None = None, recv_scales: np.ndarray | None = None):
+    """x_bits: uint16 [T,H] bf16 patterns.  Returns (recv_x, recv_scales).
+
+    recv_x is uint8 [N,H] (FP8 codes) or uint16 [N,H] (BF16); rows that no pair
+    addresses keep the contents of the arrays passed in (zeros by default)."""
+    x_bits = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    pos = np.ascontiguousarray(pos, dtype=np.int32)
+    T, H = x_bits.shape
+    k = pos.shape[1]
+    N = num_recv_rows
+    if recv_x is None:
+        recv_x = np.zeros((N, H), dtype=np.uint8 if dtype == FP8 else np.uint16)
+    if dtype == FP8 and recv_scales is None:
+        recv_scales = np.zeros((N, H // 128), dtype=np.float32)
+    sc = _p(recv_scales) if recv_scales is not None else None
+    rc = lib().orc_dispatch(T, H, k, N, dtype, _p(x_bits), _p(pos), _p(recv_x), sc)
+    if rc != 0:
+        raise ValueError("oracle dispatch: invalid arguments")
+    return recv_x, recv_scales
+
+
+def combine(y_bits: np.ndarray, pos: np.ndarray, w: np.ndarray) -> np.ndarray:
+    """y_bits: uint16 [N,H] bf16 patterns.  Returns uint16 [T,H] bf16 patterns."""
+    y_bits = np.ascontiguousarray(y_bits, dtype=np.uint16)
+    pos = np.ascontiguousarray(pos, dtype=np.int32)
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    N, H = y_bits.shape
+    T, k = pos.shape
+    out = np.empty((T, H), dtype=np.uint16)
+    rc = lib().orc_combine(T, H, k, N, _p(y_bits), _p(pos), _p(w), _p(out))
+    if rc != 0:
+        raise ValueError("oracle combine: invalid arguments")
+    return out

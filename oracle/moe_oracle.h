@@ -1,0 +1,83 @@
+/*
+ * moe_oracle.h -- plain, slow, single-threaded CPU oracle for MoE dispatch/combine.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the CPU-baseline
+ * leg of the benchmark may load this library.  The product path never calls it,
+ * and it shares no source, header, table or helper with the HIP library.
+ *
+ * Every function is the plain definition (or the written recipe) of one step:
+ *   - route:    "Efficient and Portable Mixture-of-Experts Communication"
+ *               (Perplexity), section "Introduction" (router -> probability
+ *               distribution -> top-K experts -> weighted sum), and
+ *               "DeepSeek, DeepEP open-sourced" (GeekNews 19421), topic body
+ *               (group-limited gating; top-4 groups then top-8 experts in the
+ *               "Performance > Normal kernels" workload).
+ *   - layout:   Perplexity page, sections "Portable kernels" and "Dispatch"
+ *               (per-expert counts; unique receive addresses; source index kept
+ *               for combine), DeepEP V2 digest, section "training/prefill/decoding
+ *               usage" (per-expert token counts for the GEMM).
+ *   - dispatch: Perplexity page, section "Dispatch" (tokens plus block scaling
+ *               factors into contiguous per-expert buffers); FP8 dispatch of the
+ *               DeepEP V1/V2 performance workloads.
+ *   - combine:  Perplexity page, section "Combine" (weighted average of the expert
+ *               contributions, 16-bit activations).
+ *
+ * Readings where the pages are silent (group score, tie-breaks, slot order, exp
+ * recipe, scale definition, receive order, ...) are the ones listed in the design
+ * notes; each function below states the reading it applies.
+ *
+ * Conventions: all arrays row-major, caller-owned; bf16 values travel as uint16
+ * bit patterns; return 0 on success, -1 on an invalid argument.
+ */
+#ifndef MOE_ORACLE_H
+#define MOE_ORACLE_H
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* exp recipe (Cody-Waite reduction + degree-7 Taylor), fp32. */
+float orc_exp_r(float z);
+/* 1 / (1 + exp_r(-x)), fp32, correctly rounded division. */
+float orc_sigmoid(float x);
+void orc_exp_r_array(const float* z, float* out, int64_t n);
+void orc_sigmoid_array(const float* x, float* out, int64_t n);
+
+/* OCP E4M3FN: value of a code (NaN for 0x7F/0xFF). */
+double orc_e4m3_value(uint8_t code);
+/* nearest E4M3FN code, ties to even, magnitudes above 448 saturate, sign kept. */
+uint8_t orc_e4m3_from_f32(float y);
+void orc_e4m3_from_f32_array(const float* y, uint8_t* out, int64_t n);
+/* bf16 nearest-even of a double (single rounding). */
+uint16_t orc_bf16_from_f64(double v);
+void orc_bf16_from_f64_array(const double* v, uint16_t* out, int64_t n);
+
+/* score_fn: 0 = sigmoid, 1 = softmax.  group_topn: experts summed per group score
+   (0 selects topk / topk_group).  Outputs idx [T,k] int32, w [T,k] fp32. */
+int orc_route(int T, int E, int G, int g, int k, int group_topn, int score_fn,
+              int renormalize, const float* logits, int32_t* idx, float* w);
+
+/* capacity C = 0: compact receive buffer, N = T*k rows.
+   capacity C > 0: padded, N = E*C rows, expert e owns rows [e*C, e*C + C).
+   Outputs: cnt_e[E], cnt_r[R], off_e[E+1], off_r[R+1], pos[T,k], recv_src[N],
+   overflow[1]. */
+int orc_layout(int T, int E, int k, int R, int C, const int32_t* idx,
+               int32_t* cnt_e, int32_t* cnt_r, int32_t* off_e, int32_t* off_r,
+               int32_t* pos, int32_t* recv_src, int32_t* overflow);
+
+/* dtype 0: FP8 E4M3FN with one fp32 scale per 128 channels (recv_x bytes [N,H],
+   recv_scales [N,H/128]); dtype 1: BF16 copy (recv_x as uint16 [N,H]).
+   Rows whose pos is -1 are skipped; rows never addressed are left untouched. */
+int orc_dispatch(int T, int H, int k, int N, int dtype, const uint16_t* x,
+                 const int32_t* pos, void* recv_x, float* recv_scales);
+
+/* out[t,c] = bf16( sum_j w[t,j] * y[pos[t,j], c] ), sum in double; pos -1
+   contributes nothing. */
+int orc_combine(int T, int H, int k, int N, const uint16_t* y, const int32_t* pos,
+                const float* w, uint16_t* out);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,603 @@
+"""Pins for the CPU oracle: it is checked against things other than itself.
+
+Each test fixes the oracle to a closed form, a brute-force enumeration, a
+library routine, a hand-worked fixture under tests/golden/, or an invariant the
+method must satisfy, chosen so that a plausible slip (a dropped term, a wrong
+sign or index, a transposed operand, max instead of sum, a different tie rule)
+fails at least one of them.  No GPU is used here.
+"""
+import ctypes
+import itertools
+import json
+import math
+import os
+import subprocess
+
+import numpy as np
+import pytest
+
+import workloads as W
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+HELPERS = os.path.join(os.path.dirname(__file__), "helpers")
+
+
+def golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def ulp32(x):
+    x = np.abs(np.asarray(x, dtype=np.float64))
+    e = np.floor(np.log2(np.maximum(x, 2.0 ** -126)))
+    return 2.0 ** (e - 23)
+
+
+# --------------------------------------------------------------------------
+# exp recipe and sigmoid
+# --------------------------------------------------------------------------
+def test_exp_r_accuracy_dense_sweep(orc):
+    """Within 1 ulp of exp over [-80, 80] (closed form: the true exponential)."""
+    z = np.concatenate([
+        np.linspace(-79.999, 79.999, 2_000_001, dtype=np.float32),
+        np.random.default_rng(5).uniform(-2, 2, 1_000_000).astype(np.float32),
+        np.float32([0.0, -0.0, 1e-30, -1e-30, 0.34657359, -0.34657359]),
+    ])
+    got = orc.exp_r(z).astype(np.float64)
+    ref = np.exp(z.astype(np.float64))
+    err = np.abs(got - ref) / ulp32(ref)
+    assert err.max() <= 1.0, err.max()
+
+
+def test_exp_r_clamp_and_exact_points(orc):
+    assert orc.exp_r(np.float32([80.0]))[0] == np.inf
+    assert orc.exp_r(np.float32([1000.0]))[0] == np.inf
+    assert orc.exp_r(np.float32([-80.0]))[0] == 0.0
+    assert orc.exp_r(np.float32([0.0]))[0] == 1.0
+    # results stay normal right up to the clamp
+    v = orc.exp_r(np.float32([-79.99]))[0]
+    assert v >= np.finfo(np.float32).tiny
+    # the scaling by 2^n is exact: exp(z) / exp(z - n ln2) is 2^n when both
+    # arguments are exact in fp32 (z - 16*ln2_hi is exact for these z)
+    for z in np.float32([3.0, -7.5, 20.25, -40.125]):
+        zz = np.float32(z - np.float32(16 * 0.693145751953125))
+        a = float(orc.exp_r(np.float32([z]))[0])
+        b = float(orc.exp_r(np.float32([zz]))[0])
+        assert abs(a / b / 2 ** 16 - math.exp(16 * 0.693145751953125 - 16 * math.log(2))) < 3e-7
+
+
+def test_sigmoid_accuracy_and_specials(orc):
+    x = np.concatenate([np.linspace(-79.9, 79.9, 1_000_001, dtype=np.float32),
+                        np.random.default_rng(6).standard_normal(500_000).astype(np.float32)])
+    got = orc.sigmoid(x).astype(np.float64)
+    ref = 1.0 / (1.0 + np.exp(-x.astype(np.float64)))
+    err = np.abs(got - ref) / ulp32(ref)
+    # exp error (< 1 ulp) + rounding of 1 + e (half an ulp, relative) + the
+    # division (half an ulp) + an ulp-scale step at powers of two
+    assert err.max() <= 2.5, err.max()
+    assert orc.sigmoid(np.float32([0.0]))[0] == 0.5
+    assert orc.sigmoid(np.float32([80.0]))[0] == 1.0
+    assert orc.sigmoid(np.float32([-80.0]))[0] == 0.0
+    # monotone non-decreasing
+    xs = np.sort(np.random.default_rng(7).uniform(-20, 20, 200_000).astype(np.float32))
+    assert np.all(np.diff(orc.sigmoid(xs)) >= 0)
+
+
+# --------------------------------------------------------------------------
+# E4M3FN codec
+# --------------------------------------------------------------------------
+def test_e4m3_values_match_ocp_table(orc):
+    g = golden("e4m3_ocp_values.json")
+    for code, val in g["values"]:
+        got = orc.e4m3_value(int(code, 16))
+        assert got == val and math.copysign(1, got) == math.copysign(1, val), code
+    for code in g["nan_codes"]:
+        assert math.isnan(orc.e4m3_value(int(code, 16)))
+    vals = [orc.e4m3_value(c) for c in range(127)]
+    assert all(a < b for a, b in zip(vals, vals[1:]))        # codes are ordered
+    assert len(set(vals)) == 127
+
+
+def test_e4m3_hand_rounding_cases(orc):
+    for val, code, why in golden("e4m3_rounding_cases.json")["cases"]:
+        got = int(orc.e4m3_from_f32(np.float32([val]))[0])
+        assert got == int(code, 16), (val, code, hex(got), why)
+
+
+def _build_checker():
+    src = os.path.join(HELPERS, "e4m3_check.c")
+    out = os.path.join(HELPERS, "libe4m3check.so")
+    if not os.path.exists(out) or os.path.getmtime(out) < os.path.getmtime(src):
+        tmp = out + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O2", "-fopenmp", "-shared", "-fPIC", "-o", tmp, src, "-lm"])
+        os.replace(tmp, out)
+    L = ctypes.CDLL(out)
+    L.check_fn.restype = ctypes.c_int64
+    L.check_fn.argtypes = [ctypes.c_uint32, ctypes.c_uint32, ctypes.c_void_p,
+                           ctypes.POINTER(ctypes.c_uint32)]
+    L.check_codes.restype = ctypes.c_int64
+    L.check_codes.argtypes = [ctypes.c_uint32, ctypes.c_int64, ctypes.c_void_p,
+                              ctypes.POINTER(ctypes.c_uint32)]
+    return L
+
+
+def test_e4m3_exhaustive_neighbour_check(orc):
+    """Every fp32 pattern up to 2^9 in magnitude, both signs: the oracle's code is
+    the nearest-even (saturating) one, by an independent neighbour test."""
+    chk = _build_checker()
+    fn = ctypes.cast(orc.lib().orc_e4m3_from_f32, ctypes.c_void_p)
+    first = ctypes.c_uint32()
+    hi = 0x44000000  # 512.0
+    assert chk.check_fn(0, hi, fn, ctypes.byref(first)) == 0, hex(first.value)
+    assert chk.check_fn(0x80000000, 0x80000000 + hi, fn, ctypes.byref(first)) == 0, hex(first.value)
+
+
+def test_e4m3_matches_torch_cast(orc):
+    """Library cross-check: torch's float8_e4m3fn cast is nearest-even; equal for |y| <= 448."""
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(8)
+    y = np.concatenate([
+        rng.uniform(-448, 448, 2_000_000).astype(np.float32),
+        (rng.standard_normal(1_000_000) * 0.05).astype(np.float32),
+        W.bf16_bits_to_f32(np.arange(0, 1 << 16, dtype=np.uint16)),
+    ])
+    y = y[np.isfinite(y) & (np.abs(y) <= 448)]
+    ref = torch.from_numpy(y).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = orc.e4m3_from_f32(y)
+    assert np.array_equal(got, ref)
+
+
+# --------------------------------------------------------------------------
+# bf16 rounding
+# --------------------------------------------------------------------------
+def test_bf16_matches_torch_on_fp32_inputs(orc):
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(9)
+    f = np.concatenate([rng.standard_normal(1_000_000).astype(np.float32),
+                        (rng.standard_normal(100_000) * 1e-38).astype(np.float32),
+                        np.float32([0.0, -0.0, 3.0e38, -3.0e38, 1e-45])])
+    ref = torch.from_numpy(f).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = orc.bf16_from_f64(f.astype(np.float64))
+    assert np.array_equal(got, ref)
+
+
+def test_bf16_single_rounding_from_double(orc):
+    # 1 + 2^-8 + 2^-40 is just above the midpoint of 1 and 1 + 2^-7: the correct
+    # bf16 is 1 + 2^-7 (0x3f81); rounding through fp32 first would give 1.0.
+    assert orc.bf16_from_f64(np.float64([1 + 2 ** -8 + 2 ** -40]))[0] == 0x3F81
+    assert orc.bf16_from_f64(np.float64([1 + 2 ** -8]))[0] == 0x3F80
+    assert orc.bf16_from_f64(np.float64([-(1 + 3 * 2 ** -8)]))[0] == 0xBF82
+    assert orc.bf16_from_f64(np.float64([2.0 ** 128]))[0] == 0x7F80
+
+
+# --------------------------------------------------------------------------
+# route
+# --------------------------------------------------------------------------
+def _ahead_key(s, i):
+    return (-float(s), i)
+
+
+def _brute_route(s, G, g, k, n):
+    """Enumerates every group subset and every expert subset (not the oracle's
+    repeated-argmax procedure) and returns the lexicographically best choice."""
+    E = len(s)
+    Eg = E // G
+    order = lambda ids: sorted(ids, key=lambda e: _ahead_key(s[e], e))  # noqa: E731
+    gsc = []
+    for gr in range(G):
+        top = order(range(gr * Eg, (gr + 1) * Eg))[:n]
+        acc = np.float32(s[top[0]])
+        for e in top[1:]:
+            acc = np.float32(acc + np.float32(s[e]))
+        gsc.append(acc)
+    best_groups = None
+    for sub in itertools.combinations(range(G), g):
+        key = sorted([_ahead_key(gsc[x], x) for x in sub])
+        if best_groups is None or key < best_groups[0]:
+            best_groups = (key, set(sub))
+    cand = [e for e in range(E) if e // Eg in best_groups[1]]
+    best = None
+    for sub in itertools.combinations(cand, k):
+        key = sorted([_ahead_key(s[e], e) for e in sub])
+        if best is None or key < best[0]:
+            best = (key, sub)
+    return order(best[1])
+
+
+@pytest.mark.parametrize("E,G,g,k,n", [(8, 4, 2, 2, 0), (16, 4, 2, 2, 0), (16, 4, 2, 4, 2),
+                                       (12, 3, 2, 3, 1), (16, 8, 3, 4, 2), (16, 2, 1, 3, 3),
+                                       (8, 1, 1, 3, 0), (16, 16, 4, 4, 1)])
+@pytest.mark.parametrize("ties", [False, True])
+def test_route_brute_force(orc, E, G, g, k, n, ties):
+    rng = np.random.default_rng(E * 100 + G * 10 + k + (1000 if ties else 0))
+    T = 24
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    if ties:
+        logits = W.tie_heavy(logits * 0.4)
+        logits[0, :] = 0.0
+        logits[1, ::2] = -0.0
+    idx, w = orc.route(logits, G, g, k, group_topn=n)
+    nn = n if n > 0 else max(1, k // g)
+    s = orc.sigmoid(logits)
+    for t in range(T):
+        assert list(idx[t]) == _brute_route(s[t], G, g, k, nn if G > 1 else 1), t
+
+
+def test_route_golden_group_score_reading(orc):
+    gdat = golden("route_group_score.json")
+    logits = np.float32(gdat["logits"])
+    for case in gdat["cases"]:
+        idx, w = orc.route(logits, gdat["num_groups"], gdat["topk_group"], gdat["topk"],
+                           group_topn=case["group_topn"])
+        assert list(idx[0]) == case["idx"], case["why"]
+        if "w" in case:
+            assert list(w[0]) == case["w"]
+    idx, _ = orc.route(logits, 1, 1, gdat["topk"])
+    assert list(idx[0]) == gdat["ungrouped"]["idx"]
+
+
+def test_route_ungrouped_is_stable_sort(orc):
+    """G = 1 (and g = G) reduce to a stable descending sort of the scores."""
+    rng = np.random.default_rng(11)
+    logits = W.tie_heavy(rng.standard_normal((200, 32)).astype(np.float32))
+    s = orc.sigmoid(logits)
+    for (G, g) in [(1, 1), (4, 4), (8, 8)]:
+        idx, _ = orc.route(logits, G, g, 32 if G == 1 else 8)
+        ref = np.argsort(-s.astype(np.float64), axis=1, kind="stable")
+        kk = idx.shape[1]
+        if G == 1:
+            assert np.array_equal(idx, ref[:, :kk])
+        else:
+            # all groups kept: same as the ungrouped top-k
+            assert np.array_equal(idx, ref[:, :kk])
+
+
+def test_route_k1_is_argmax(orc):
+    rng = np.random.default_rng(12)
+    logits = W.tie_heavy(rng.standard_normal((300, 64)).astype(np.float32))
+    idx, w = orc.route(logits, 1, 1, 1)
+    assert np.array_equal(idx[:, 0], np.argmax(orc.sigmoid(logits), axis=1))
+    assert np.all(w == 1.0)
+    idx, w = orc.route(logits, 1, 1, 1, score_fn=orc.SOFTMAX)
+    assert np.array_equal(idx[:, 0], np.argmax(logits, axis=1))
+    assert np.all(w == 1.0)
+
+
+def test_route_matches_torch_topk_distinct(orc):
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(13)
+    logits = rng.standard_normal((500, 64)).astype(np.float32)
+    s = orc.sigmoid(logits)
+    assert all(len(set(r)) == len(r) for r in s)
+    idx, w = orc.route(logits, 1, 1, 6)
+    vals, ref = torch.topk(torch.from_numpy(s), 6, dim=1)
+    assert np.array_equal(idx, ref.numpy())
+    sel = vals.double().numpy()
+    assert np.allclose(w, sel / sel.sum(1, keepdims=True), rtol=3e-7, atol=0)
+
+
+def test_route_softmax_top2_closed_form(orc):
+    """Mixtral-shaped: renormalised softmax over two experts is 1/(1+e^(l1-l0))."""
+    wl = W.get("mixtral").replace(T=4096)
+    logits = W.gen_logits(wl)
+    idx, w = orc.route(logits, 1, 1, 2, score_fn=orc.SOFTMAX)
+    l0 = np.take_along_axis(logits, idx[:, :1], 1)[:, 0].astype(np.float64)
+    l1 = np.take_along_axis(logits, idx[:, 1:2], 1)[:, 0].astype(np.float64)
+    ref0 = 1.0 / (1.0 + np.exp(l1 - l0))
+    assert np.all(np.abs(w[:, 0] - ref0) <= 4 * ulp32(ref0))
+    assert np.all(np.abs(w[:, 1] - (1 - ref0)) <= 4 * ulp32(ref0))
+    assert np.all(l0 >= l1)
+
+
+def test_route_softmax_unnormalised_is_full_softmax(orc):
+    rng = np.random.default_rng(14)
+    logits = rng.standard_normal((100, 8)).astype(np.float32)
+    idx, w = orc.route(logits, 1, 1, 2, score_fn=orc.SOFTMAX, renormalize=False)
+    l = logits.astype(np.float64)
+    p = np.exp(l - l.max(1, keepdims=True))
+    p /= p.sum(1, keepdims=True)
+    ref = np.take_along_axis(p, idx, 1)
+    assert np.all(np.abs(w - ref) <= 8 * ulp32(ref))
+
+
+def test_route_sigmoid_unnormalised_weights_are_scores(orc):
+    rng = np.random.default_rng(15)
+    logits = rng.standard_normal((50, 16)).astype(np.float32)
+    idx, w = orc.route(logits, 4, 2, 3, renormalize=False)
+    assert np.array_equal(w, np.take_along_axis(orc.sigmoid(logits), idx, 1))
+
+
+@pytest.mark.parametrize("name", ["dsv3_prefill", "skewed_8k", "tiny"])
+def test_route_invariants_full_size(orc, name):
+    wl = W.get(name)
+    logits = W.gen_logits(wl)
+    idx, w = orc.route(logits, wl.G, wl.g, wl.k)
+    s = orc.sigmoid(logits)
+    T, k = idx.shape
+    assert np.all((idx >= 0) & (idx < wl.E))
+    srt = np.sort(idx, 1)
+    assert np.all(srt[:, 1:] != srt[:, :-1])                       # distinct
+    ngroups = np.array([len(set(r)) for r in idx // (wl.E // wl.G)])
+    assert np.all(ngroups <= wl.g)                                  # group-limited
+    sel = np.take_along_axis(s, idx, 1)
+    assert np.all(sel[:, :-1] >= sel[:, 1:])                        # descending slots
+    assert np.all((w >= 0) & (w <= 1))
+    assert np.all(np.abs(w.astype(np.float64).sum(1) - 1) <= k * 2 ** -23)
+
+
+def test_route_bad_arguments(orc):
+    x = np.zeros((2, 8), np.float32)
+    for args in [(3, 1, 2), (4, 5, 2), (4, 2, 5), (4, 0, 2)]:
+        with pytest.raises(ValueError):
+            orc.route(x, *args)
+
+
+def test_skew_calibration(orc):
+    """The skewed workload's hottest expert carries 10 +- 0.5 x the mean load."""
+    wl = W.get("skewed_8k")
+    idx, _ = orc.route(W.gen_logits(wl), wl.G, wl.g, wl.k)
+    load = np.bincount(idx.ravel(), minlength=wl.E)
+    ratio = load.max() / (wl.T * wl.k / wl.E)
+    assert 9.5 <= ratio <= 10.5, ratio
+
+
+# --------------------------------------------------------------------------
+# layout
+# --------------------------------------------------------------------------
+def _random_idx(rng, T, E, k, skew=False):
+    if skew:
+        p = (np.arange(E) + 1.0) ** -1.5
+        p /= p.sum()
+    out = np.empty((T, k), np.int32)
+    for t in range(T):
+        out[t] = rng.choice(E, size=k, replace=False, p=p if skew else None)
+    return out
+
+
+@pytest.mark.parametrize("T,E,k,R", [(1, 4, 1, 1), (64, 16, 2, 4), (333, 256, 8, 32),
+                                     (1000, 8, 2, 8), (77, 32, 4, 2)])
+@pytest.mark.parametrize("skew", [False, True])
+def test_layout_compact(orc, T, E, k, R, skew):
+    rng = np.random.default_rng(T + E + k)
+    idx = _random_idx(rng, T, E, k, skew)
+    L = orc.layout(idx, E, R)
+    assert L["flags"] == 0
+    assert np.array_equal(L["cnt_e"], np.bincount(idx.ravel(), minlength=E))
+    assert L["cnt_e"].sum() == T * k
+    Er = E // R
+    ref_r = np.zeros(R, np.int64)
+    for t in range(T):
+        for r in set(int(e) // Er for e in idx[t]):
+            ref_r[r] += 1
+    assert np.array_equal(L["cnt_r"], ref_r)
+    assert T <= L["cnt_r"].sum() <= T * min(k, R)
+    assert np.array_equal(L["off_e"], np.concatenate([[0], np.cumsum(L["cnt_e"])]))
+    assert np.array_equal(L["off_r"], L["off_e"][::Er])
+    # stable counting sort == numpy's stable argsort of the flattened indices
+    assert np.array_equal(L["recv_src"], np.argsort(idx.ravel(), kind="stable"))
+    flat = L["pos"].ravel()
+    assert np.array_equal(np.sort(flat), np.arange(T * k))         # a permutation
+    assert np.array_equal(L["recv_src"][flat], np.arange(T * k))   # inverse maps
+    # rows of each expert region hold that expert, in increasing token order
+    src_e = idx.ravel()[L["recv_src"]]
+    assert np.all(np.diff(src_e) >= 0)
+    for e in range(E):
+        toks = L["recv_src"][L["off_e"][e]:L["off_e"][e + 1]] // k
+        assert np.all(np.diff(toks) > 0)
+
+
+@pytest.mark.parametrize("C", [1, 3, 8, 64])
+def test_layout_padded(orc, C):
+    rng = np.random.default_rng(C)
+    T, E, k, R = 128, 16, 4, 4
+    idx = _random_idx(rng, T, E, k, skew=True)
+    L = orc.layout(idx, E, R, capacity=C)
+    cnt = np.bincount(idx.ravel(), minlength=E)
+    assert np.array_equal(L["cnt_e"], cnt)                       # unclamped
+    assert L["flags"] == (1 if cnt.max() > C else 0)
+    order = np.argsort(idx.ravel(), kind="stable")
+    off = np.concatenate([[0], np.cumsum(cnt)])
+    ref_src = np.full(E * C, -1, np.int32)
+    ref_pos = np.full(T * k, -1, np.int32)
+    for e in range(E):
+        pairs = order[off[e]:off[e + 1]][:C]
+        ref_src[e * C:e * C + len(pairs)] = pairs
+        ref_pos[pairs] = e * C + np.arange(len(pairs))
+    assert np.array_equal(L["recv_src"], ref_src)
+    assert np.array_equal(L["pos"].ravel(), ref_pos)
+
+
+def test_layout_invalid_indices_flagged(orc):
+    idx = np.array([[0, 1], [2, 2]], np.int32)
+    assert orc.layout(idx, 4, 2)["flags"] & 2
+    idx = np.array([[0, 4], [2, 3]], np.int32)
+    assert orc.layout(idx, 4, 2)["flags"] & 2
+    idx = np.array([[0, -1], [2, 3]], np.int32)
+    assert orc.layout(idx, 4, 2)["flags"] & 2
+
+
+def test_layout_empty(orc):
+    L = orc.layout(np.zeros((0, 8), np.int32), 256, 32)
+    assert L["cnt_e"].sum() == 0 and L["off_e"][-1] == 0 and L["flags"] == 0
+
+
+# --------------------------------------------------------------------------
+# dispatch
+# --------------------------------------------------------------------------
+def _dsv3_small(T=96, H=1024, E=32, k=4):
+    wl = W.custom(T=T, H=H, E=E, G=4, g=2, k=k, score="sigmoid", R=4, dtype="fp8")
+    return wl
+
+
+def test_dispatch_every_nonzero_block_hits_448(orc):
+    wl = _dsv3_small()
+    x = W.gen_x(wl)
+    x[3, :128] = 0                        # an all-zero block
+    x[4, 128:256] = 0x8000                # -0.0 block
+    idx, _ = orc.route(W.gen_logits(wl), wl.G, wl.g, wl.k)
+    L = orc.layout(idx, wl.E, wl.R)
+    q, sc = orc.dispatch(x, L["pos"], wl.N)
+    xf = W.bf16_bits_to_f32(x).reshape(wl.T, wl.S, 128)
+    amax = np.abs(xf).max(2)
+    qb = q.reshape(wl.N, wl.S, 128)
+    for t in range(wl.T):
+        for j in range(wl.k):
+            p = L["pos"][t, j]
+            has448 = np.any((qb[p] & 0x7F) == 0x7E, axis=1)
+            assert np.array_equal(has448, amax[t] > 0)
+    # zero blocks: all codes zero (sign kept), floor scale 2^-100 / 448
+    p = L["pos"][3, 0]
+    assert np.all(qb[p, 0] == 0) and sc[p, 0] == np.float32(2.0 ** -100) / np.float32(448)
+    p = L["pos"][4, 0]
+    assert np.all(qb[p, 1] == 0x80)
+
+
+def test_dispatch_dequant_error_bound(orc):
+    """|x - q*scale| <= 2^-4 |x| + 2^-10 scale + 2^-20 |x| (half an E4M3 step
+    in the normal range, half the subnormal step, slack for fp32 rounding)."""
+    wl = _dsv3_small(T=64, H=2048)
+    x = W.gen_x(wl)
+    x[5] = W.f32_to_bf16_bits(W.bf16_bits_to_f32(x[5]) * np.float32(1e-30))   # tiny values
+    x[6, 7] = W.f32_to_bf16_bits(np.float32([3e4]))[0]                       # one huge value
+    pos = np.arange(wl.T * 1, dtype=np.int32).reshape(wl.T, 1)
+    q, sc = orc.dispatch(x, pos, wl.T)
+    xf = W.bf16_bits_to_f32(x).astype(np.float64).reshape(wl.T, wl.S, 128)
+    vals = np.array([orc.e4m3_value(c) for c in range(256)])
+    deq = vals[q].reshape(wl.T, wl.S, 128) * sc.astype(np.float64)[:, :, None]
+    bound = 2 ** -4 * np.abs(xf) + 2 ** -10 * sc[:, :, None] + 2 ** -20 * np.abs(xf)
+    assert np.all(np.abs(xf - deq) <= bound)
+
+
+def test_dispatch_scale_definition(orc):
+    wl = _dsv3_small(T=32, H=512)
+    x = W.gen_x(wl)
+    pos = np.arange(wl.T, dtype=np.int32).reshape(wl.T, 1)
+    _, sc = orc.dispatch(x, pos, wl.T)
+    amax = np.abs(W.bf16_bits_to_f32(x).astype(np.float64)).reshape(wl.T, wl.S, 128).max(2)
+    # the stored scale is amax/448 correctly rounded: within half an ulp
+    assert np.all(np.abs(sc.astype(np.float64) - amax / 448) <= 0.5 * ulp32(amax / 448))
+
+
+def test_dispatch_matches_torch_quantisation(orc):
+    """Library cross-check of the codes: torch's e4m3fn cast of x * (448/amax)."""
+    torch = pytest.importorskip("torch")
+    wl = _dsv3_small(T=50, H=768)
+    x = W.gen_x(wl)
+    pos = np.arange(wl.T, dtype=np.int32).reshape(wl.T, 1)
+    q, _ = orc.dispatch(x, pos, wl.T)
+    xf = torch.from_numpy(W.bf16_bits_to_f32(x)).reshape(wl.T, wl.S, 128)
+    amax = xf.abs().amax(2, keepdim=True).clamp_min(2.0 ** -100)
+    inv = torch.tensor(448.0, dtype=torch.float32) / amax
+    ref = (xf * inv).to(torch.float8_e4m3fn).view(torch.uint8).reshape(wl.T, wl.H).numpy()
+    assert np.array_equal(q, ref)
+
+
+def test_dispatch_bf16_is_verbatim_copy(orc):
+    wl = W.get("mixtral").replace(T=256, H=512)
+    x = W.gen_x(wl)
+    idx, _ = orc.route(W.gen_logits(wl), 1, 1, 2, score_fn=orc.SOFTMAX)
+    L = orc.layout(idx, wl.E, wl.R)
+    rx, _ = orc.dispatch(x, L["pos"], wl.N, dtype=orc.BF16)
+    assert np.array_equal(rx, x[L["recv_src"] // wl.k])
+
+
+def test_dispatch_rows_follow_layout(orc):
+    wl = _dsv3_small(T=40, H=256, E=16, k=3)
+    x = W.gen_x(wl)
+    idx, _ = orc.route(W.gen_logits(wl), wl.G, wl.g, wl.k)
+    L = orc.layout(idx, wl.E, wl.R)
+    q, sc = orc.dispatch(x, L["pos"], wl.N)
+    single, ssc = orc.dispatch(x, np.arange(wl.T, dtype=np.int32)[:, None], wl.T)
+    src_t = L["recv_src"] // wl.k
+    assert np.array_equal(q, single[src_t])
+    assert np.array_equal(sc, ssc[src_t])
+
+
+# --------------------------------------------------------------------------
+# combine
+# --------------------------------------------------------------------------
+def test_combine_golden(orc):
+    for case in golden("combine_cases.json")["cases"]:
+        y = W.f32_to_bf16_bits(np.float32(case["y"]))
+        assert np.array_equal(W.bf16_bits_to_f32(y), np.float32(case["y"]))
+        k = len(case["w"])
+        out = orc.combine(y, np.arange(k, dtype=np.int32)[None, :], np.float32([case["w"]]))
+        got = W.bf16_bits_to_f32(out)[0]
+        assert np.array_equal(got, np.float32(case["out"])), (got, case)
+        assert np.array_equal(np.signbit(got), np.signbit(np.float32(case["out"])))
+
+
+def test_roundtrip_bf16_identity_experts(orc):
+    """Dispatch (BF16) -> identity experts -> combine with weights summing to 1 returns x."""
+    for name in ["mixtral", "dsv3_prefill"]:
+        wl = W.get(name).replace(T=128, H=512)
+        x = W.gen_x(wl)
+        sf = orc.SOFTMAX if wl.score == "softmax" else orc.SIGMOID
+        idx, w = orc.route(W.gen_logits(wl), wl.G, wl.g, wl.k, score_fn=sf)
+        L = orc.layout(idx, wl.E, wl.R)
+        rx, _ = orc.dispatch(x, L["pos"], wl.N, dtype=orc.BF16)
+        out = orc.combine(rx, L["pos"], w)
+        assert np.array_equal(out, x)
+
+
+def test_roundtrip_fp8_within_quantisation_bound(orc):
+    wl = W.get("dsv3_prefill").replace(T=128, H=1024)
+    x = W.gen_x(wl)
+    idx, w = orc.route(W.gen_logits(wl), wl.G, wl.g, wl.k)
+    L = orc.layout(idx, wl.E, wl.R)
+    q, sc = orc.dispatch(x, L["pos"], wl.N)
+    vals = np.array([orc.e4m3_value(c) for c in range(256)])
+    deq = vals[q].reshape(wl.N, wl.S, 128) * sc.astype(np.float64)[:, :, None]
+    y = orc.bf16_from_f64(deq.reshape(wl.N, wl.H))
+    out = W.bf16_bits_to_f32(orc.combine(y, L["pos"], w)).astype(np.float64)
+    xf = W.bf16_bits_to_f32(x).astype(np.float64)
+    blk_amax = np.repeat(np.abs(xf).reshape(wl.T, wl.S, 128).max(2), 128, axis=1)
+    bound = (2 ** -4 + 2 ** -8) * np.abs(xf) + 2 ** -8 * np.abs(out) + 2 ** -10 * blk_amax / 448
+    assert np.all(np.abs(out - xf) <= bound + 1e-30)
+
+
+def test_combine_k1_unit_weight_is_exact_copy(orc):
+    rng = np.random.default_rng(21)
+    y = W.f32_to_bf16_bits(rng.standard_normal((50, 64)).astype(np.float32))
+    pos = rng.permutation(50).astype(np.int32)[:, None]
+    out = orc.combine(y, pos, np.ones((50, 1), np.float32))
+    assert np.array_equal(out, y[pos[:, 0]])
+
+
+def test_combine_linear_in_weights(orc):
+    rng = np.random.default_rng(22)
+    T, k, H = 40, 4, 128
+    y = W.f32_to_bf16_bits(rng.standard_normal((T * k, H)).astype(np.float32))
+    pos = rng.permutation(T * k).astype(np.int32).reshape(T, k)
+    w = rng.uniform(0, 1, (T, k)).astype(np.float32)
+    a = W.bf16_bits_to_f32(orc.combine(y, pos, w))
+    b = W.bf16_bits_to_f32(orc.combine(y, pos, w * np.float32(4)))
+    assert np.array_equal(b, a * 4)
+    # swapping slots (a permutation of the pairs) leaves the sum unchanged
+    perm = np.array([2, 0, 3, 1])
+    c = W.bf16_bits_to_f32(orc.combine(y, pos[:, perm], w[:, perm]))
+    assert np.array_equal(a, c)
+
+
+def test_combine_dropped_pairs_contribute_nothing(orc):
+    rng = np.random.default_rng(23)
+    y = W.f32_to_bf16_bits(rng.standard_normal((8, 16)).astype(np.float32))
+    pos = np.array([[0, -1], [3, 5]], np.int32)
+    w = np.float32([[1.0, 0.5], [1.0, 0.0]])
+    out = orc.combine(y, pos, w)
+    assert np.array_equal(out[0], y[0])
+    assert np.array_equal(out[1], y[3])
+
+
+def test_workloads_follow_pages():
+    for it in golden("workloads_from_pages.json")["items"]:
+        wl = W.get(it["workload"])
+        assert wl.T == it["tokens"]
+        if "hidden" in it:
+            assert wl.H == it["hidden"]
+        if "topk" in it:
+            assert wl.k == it["topk"]
+        if "topk_group" in it:
+            assert wl.g == it["topk_group"]
+        if "dispatch" in it:
+            assert wl.dtype == it["dispatch"]
