@@ -1,0 +1,239 @@
+"""Benchmark of the MoE dispatch/combine hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of synthetic input:
+route (group-limited top-k) -> layout -> FP8 dispatch -> BF16 combine, on the
+DeepSeek-V3-shaped prefill workload (4096 tokens x hidden 7168, 256 experts in
+8 groups, top-4 groups then top-8 experts, 32 virtual ranks).  The expert MLP
+is not on this path: the combine reads synthetic expert outputs y [T*k, H].
+
+Inputs sit in HBM before the timed region; two input sets alternate between
+steps so no input is re-read from the 256 MB last-level cache.  Before the
+timed region the GPU is held by a short spin kernel while all K steps are
+enqueued, so the timeline holds only GPU work.  HIP events on the launch
+stream bracket every stage of every timed step.
+
+Prints one JSON line.  ``value`` is the effective HBM bandwidth of dispatch +
+combine: their algorithmic bytes over their measured time.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads as W  # noqa: E402
+
+HBM_PEAK_GBPS = 8000.0   # MI355X HBM3E, published
+METRIC = "dispatch+combine µs and effective HBM GB/s (% of peak), 4096 tok×7168 top-8"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="dsv3_prefill", choices=sorted(W.WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-reps", type=int, default=0, help="oracle repetitions (0: about 10 s)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also time a plain 1 GiB device copy (reference for counters and peak)")
+    return ap.parse_args()
+
+
+def source_digest(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "combine_group_limited_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel: str, digest: str):
+    """HBM bytes per launch measured with rocprofv3 counters (profiles/traffic.json),
+    only while the kernel's sources are unchanged since the measurement."""
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        data = json.load(f)
+    ent = data.get(kernel)
+    if not ent or ent.get("source_digest") != digest:
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def cpu_baseline(wl, reps: int):
+    """The oracle (plain single-threaded C) on the same workload, timed on the host."""
+    import oracle
+    x, logits, y = W.gen_x(wl), W.gen_logits(wl), W.gen_y(wl)
+    t_dc = 0.0
+    n = 0
+    t_start = time.perf_counter()
+    while True:
+        idx, w = oracle.route(logits, wl.G, wl.g, wl.k)
+        lay = oracle.layout(idx, wl.E, wl.R, wl.capacity)
+        t0 = time.perf_counter()
+        oracle.dispatch(x, lay["pos"], wl.N)
+        oracle.combine(y, lay["pos"], w)
+        t_dc += time.perf_counter() - t0
+        n += 1
+        if (reps and n >= reps) or (not reps and time.perf_counter() - t_start >= 10.0):
+            break
+    b = W.algorithmic_bytes(wl)
+    gbps = (b["dispatch"] + b["combine"]) * n / t_dc / 1e9
+    return {"value": round(gbps, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{n} full passes of the {wl.name} workload ({wl.T} tokens) through the oracle; "
+                      f"dispatch+combine {t_dc / n * 1e3:.1f} ms per pass, single thread",
+            "dispatch_plus_combine_ms": round(t_dc / n * 1e3, 3)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): this build has no "
+              "inter-GPU transport; run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import combine_group_limited_amd as moe
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wl = W.get(args.workload)
+    fp8 = wl.dtype == "fp8"
+
+    # ---- inputs (two sets), outputs and workspace, all resident in HBM ----
+    sets = []
+    x0 = torch.from_numpy(W.gen_x(wl).view(np.int16)).to(dev).view(torch.bfloat16)
+    l0 = torch.from_numpy(W.gen_logits(wl)).to(dev)
+    y0 = torch.from_numpy(W.gen_y(wl).view(np.int16)).to(dev).view(torch.bfloat16)
+    sets.append((x0, l0, y0))
+    g = torch.Generator(device=dev)
+    g.manual_seed(wl.seed + 1000)
+    x1 = torch.randn(x0.shape, generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    l1 = torch.randn(l0.shape, generator=g, device=dev, dtype=torch.float32)
+    if wl.skew:
+        l1 += torch.from_numpy(W.zipf_bias(wl)).to(dev)[None, :]
+    y1 = torch.randn(y0.shape, generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    sets.append((x1, l1, y1))
+
+    idx = torch.empty((wl.T, wl.k), dtype=torch.int32, device=dev)
+    wts = torch.empty((wl.T, wl.k), dtype=torch.float32, device=dev)
+    lay_out = moe.alloc_layout(wl.T, wl.E, wl.k, wl.R, wl.capacity, dev)
+    N = lay_out[0].num_recv_rows
+    recv_x = torch.empty((N, wl.H), dtype=torch.uint8 if fp8 else torch.bfloat16, device=dev)
+    recv_s = torch.empty((N, wl.S), dtype=torch.float32, device=dev) if fp8 else None
+    out = torch.empty((wl.T, wl.H), dtype=torch.bfloat16, device=dev)
+
+    def step(i, ev=None):
+        x, logits, y = sets[i % 2]
+        if ev: ev[0].record()
+        moe.route_topk(logits, wl.G, wl.g, wl.k, wl.score, out=(idx, wts))
+        if ev: ev[1].record()
+        lay = moe.get_layout(idx, wl.E, wl.R, wl.capacity, out=lay_out)
+        if ev: ev[2].record()
+        moe.dispatch(x, lay.pos, N, wl.dtype, recv_x, recv_s)
+        if ev: ev[3].record()
+        moe.combine(y, lay.pos, wts, out)
+        if ev: ev[4].record()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(K)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    if hasattr(torch.cuda, "_sleep"):
+        torch.cuda._sleep(int(2e7))    # hold the GPU while the host enqueues the K steps
+    t_wall = time.perf_counter()
+    start.record()
+    for i in range(K):
+        step(i, evs[i])
+    end.record()
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+
+    ms_step = start.elapsed_time(end) / K
+    stage = np.array([[e[s].elapsed_time(e[s + 1]) for s in range(4)] for e in evs])  # ms
+    st_mean = stage.mean(0) * 1e3   # us
+    route_us, layout_us, disp_us, comb_us = (float(v) for v in st_mean)
+
+    b = W.algorithmic_bytes(wl)
+    dc_bytes = b["dispatch"] + b["combine"]
+    dc_us = disp_us + comb_us
+    value = dc_bytes / (dc_us * 1e-6) / 1e9
+
+    kernels = {"dispatch": (disp_us, b["dispatch"], ("dispatch.hip", "moe_device.hpp")),
+               "combine": (comb_us, b["combine"], ("combine.hip", "moe_device.hpp"))}
+    dom = max(kernels, key=lambda k: kernels[k][0])
+    dom_us, dom_bytes, dom_src = kernels[dom]
+    achieved = dom_bytes / (dom_us * 1e-6) / 1e9
+    digest = source_digest(*dom_src)
+    roof = {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": load_traffic(dom, digest), "algorithmic_bytes": dom_bytes,
+            "avg_launch_us": round(dom_us, 2), "source_digest": digest}
+
+    res = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp32",
+        "data": "synthetic (seeded N(0,1) bf16 tokens and expert outputs, N(0,1) fp32 router logits)",
+        "config": {"workload": W.describe(wl), "tokens": wl.T, "hidden": wl.H, "experts": wl.E,
+                   "groups": wl.G, "topk_group": wl.g, "topk": wl.k, "virtual_ranks": wl.R,
+                   "dispatch": "fp8 e4m3 1x128" if fp8 else "bf16",
+                   "combine": "bf16 (fp32 accumulate)", "parallelism": "single GPU"},
+        "dispatch_us": round(disp_us, 2),
+        "combine_us": round(comb_us, 2),
+        "dispatch_plus_combine_us": round(dc_us, 2),
+        "route_us": round(route_us, 2),
+        "layout_us": round(layout_us, 2),
+        "dispatch_gbps": round(b["dispatch"] / (disp_us * 1e-6) / 1e9, 1),
+        "combine_gbps": round(b["combine"] / (comb_us * 1e-6) / 1e9, 1),
+        "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
+        "step_effective_gbps": round(b["total"] / (ms_step * 1e-3) / 1e9, 1),
+        "p10_p90_dispatch_plus_combine_us": [round(float(v), 2) for v in np.percentile(
+            (stage[:, 2] + stage[:, 3]) * 1e3, [10, 90])],
+        "wall_s_timed_region": round(t_wall, 4),
+        "roofline": roof,
+    }
+
+    if args.copy_calibration:
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(10):
+            dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        res["device_copy_gbps"] = round(2 * n * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)
+
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(wl, args.cpu_reps)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

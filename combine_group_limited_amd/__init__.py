@@ -1,0 +1,242 @@
+"""MI355X-native MoE dispatch/combine: thin Python binding of ``libcgl_moe.so``.
+
+The four calls of the C ABI in ``include/moe.h`` -- ``route_topk``,
+``get_layout``, ``dispatch``, ``combine`` -- plus ``quantize_e4m3``.  This
+module only marshals arguments: it checks tensor shapes, dtypes and devices,
+allocates outputs with torch (device memory and the current stream are all
+torch provides here) and passes raw pointers to the library.  Every step of
+the path runs in the HIP kernels; if the library is missing this module raises
+instead of computing anything itself.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import NamedTuple, Optional
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libcgl_moe.so")
+
+MOE_OK, MOE_ERR_INVALID, MOE_ERR_WORKSPACE, MOE_ERR_UNSUPPORTED, MOE_ERR_HIP = 0, 1, 2, 4, 5
+SCORE_FNS = {"sigmoid": 0, "softmax": 1}
+DISPATCH_DTYPES = {"fp8": 0, "bf16": 1}
+FLAG_CAPACITY_OVERFLOW, FLAG_BAD_INDEX = 1, 2
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{message} (status {status})")
+        self.status = status
+
+
+class RouteCfg(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "num_tokens", "num_experts", "num_groups", "topk_group", "topk", "group_topn", "score_fn",
+        "renormalize")]
+
+
+class LayoutCfg(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "num_tokens", "num_experts", "topk", "num_ranks", "capacity")]
+
+
+class DispatchCfg(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "num_tokens", "hidden", "topk", "num_recv_rows", "dtype", "units_per_wave")]
+
+
+class CombineCfg(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "num_tokens", "hidden", "topk", "num_recv_rows", "units_per_wave")]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded HIP library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(
+                f"{LIB_PATH} is missing: build it with `python -m combine_group_limited_amd.build` "
+                "(there is no fallback implementation)")
+        L = ctypes.CDLL(LIB_PATH)
+        P, S = ctypes.c_void_p, ctypes.c_size_t
+        L.moe_route_topk.argtypes = [ctypes.POINTER(RouteCfg), P, P, P, P]
+        L.moe_layout_workspace_bytes.argtypes = [ctypes.POINTER(LayoutCfg)]
+        L.moe_layout_workspace_bytes.restype = S
+        L.moe_get_layout.argtypes = [ctypes.POINTER(LayoutCfg)] + [P] * 9 + [S, P]
+        L.moe_dispatch.argtypes = [ctypes.POINTER(DispatchCfg), P, P, P, P, P]
+        L.moe_combine.argtypes = [ctypes.POINTER(CombineCfg), P, P, P, P, P]
+        L.moe_quantize_e4m3.argtypes = [P, P, ctypes.c_int64, P]
+        for f in ("moe_route_topk", "moe_get_layout", "moe_dispatch", "moe_combine", "moe_quantize_e4m3"):
+            getattr(L, f).restype = ctypes.c_int
+        L.moe_status_string.argtypes = [ctypes.c_int]
+        L.moe_status_string.restype = ctypes.c_char_p
+        L.moe_last_error.restype = ctypes.c_char_p
+        L.moe_abi_version.restype = ctypes.c_int32
+        _lib = L
+    return _lib
+
+
+def _check(status: int):
+    if status != MOE_OK:
+        L = lib()
+        raise MoeError(status, f"{L.moe_status_string(status).decode()}: {L.moe_last_error().decode()}")
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device) -> int:
+    torch = _torch()
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _need(t, name, dtype, shape=None, device=None):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def route_topk(logits, num_groups: int, topk_group: int, topk: int, score_fn: str = "sigmoid",
+               renormalize: bool = True, group_topn: int = 0, out=None):
+    """Group-limited top-k gating.  logits fp32 [T,E] -> (idx int32 [T,k], w fp32 [T,k])."""
+    torch = _torch()
+    _need(logits, "logits", torch.float32)
+    T, E = logits.shape
+    if out is None:
+        idx = torch.empty((T, topk), dtype=torch.int32, device=logits.device)
+        w = torch.empty((T, topk), dtype=torch.float32, device=logits.device)
+    else:
+        idx, w = out
+        _need(idx, "idx", torch.int32, (T, topk), logits.device)
+        _need(w, "w", torch.float32, (T, topk), logits.device)
+    cfg = RouteCfg(T, E, num_groups, topk_group, topk, group_topn, SCORE_FNS[score_fn], int(renormalize))
+    _check(lib().moe_route_topk(ctypes.byref(cfg), _ptr(logits), _ptr(idx), _ptr(w), _stream(logits.device)))
+    return idx, w
+
+
+class Layout(NamedTuple):
+    cnt_e: object      # int32 [E]
+    cnt_r: object      # int32 [R]
+    off_e: object      # int32 [E+1]
+    off_r: object      # int32 [R+1]
+    pos: object        # int32 [T,k]
+    recv_src: object   # int32 [N]
+    flags: object      # int32 [1]
+    num_recv_rows: int
+
+
+def layout_workspace_bytes(num_tokens: int, num_experts: int, topk: int, num_ranks: int,
+                           capacity: int = 0) -> int:
+    cfg = LayoutCfg(num_tokens, num_experts, topk, num_ranks, capacity)
+    n = lib().moe_layout_workspace_bytes(ctypes.byref(cfg))
+    if n == 0:
+        raise MoeError(MOE_ERR_INVALID, lib().moe_last_error().decode())
+    return n
+
+
+def alloc_layout(num_tokens, num_experts, topk, num_ranks, capacity=0, device="cuda"):
+    """Output tensors and workspace for get_layout (reusable across calls)."""
+    torch = _torch()
+    N = num_experts * capacity if capacity > 0 else num_tokens * topk
+    i32 = dict(dtype=torch.int32, device=device)
+    lay = Layout(torch.empty(num_experts, **i32), torch.empty(num_ranks, **i32),
+                 torch.empty(num_experts + 1, **i32), torch.empty(num_ranks + 1, **i32),
+                 torch.empty((num_tokens, topk), **i32), torch.empty(N, **i32), torch.empty(1, **i32), N)
+    ws = torch.empty(layout_workspace_bytes(num_tokens, num_experts, topk, num_ranks, capacity),
+                     dtype=torch.uint8, device=device)
+    return lay, ws
+
+
+def get_layout(topk_idx, num_experts: int, num_ranks: int, capacity: int = 0, out=None) -> Layout:
+    """Routing layout (counts, offsets, receive rows).  out = (Layout, workspace) to reuse buffers."""
+    torch = _torch()
+    _need(topk_idx, "topk_idx", torch.int32)
+    T, k = topk_idx.shape
+    if out is None:
+        out = alloc_layout(T, num_experts, k, num_ranks, capacity, topk_idx.device)
+    lay, ws = out
+    cfg = LayoutCfg(T, num_experts, k, num_ranks, capacity)
+    _check(lib().moe_get_layout(ctypes.byref(cfg), _ptr(topk_idx), _ptr(lay.cnt_e), _ptr(lay.cnt_r),
+                                _ptr(lay.off_e), _ptr(lay.off_r), _ptr(lay.pos), _ptr(lay.recv_src),
+                                _ptr(lay.flags), _ptr(ws), ws.numel(), _stream(topk_idx.device)))
+    return lay
+
+
+def dispatch(x, pos, num_recv_rows: int, dtype: str = "fp8", recv_x=None, recv_scales=None,
+             units_per_wave: int = 0):
+    """x bf16 [T,H] -> (recv_x uint8 [N,H] or bf16 [N,H], recv_scales fp32 [N,H/128] or None)."""
+    torch = _torch()
+    _need(x, "x", torch.bfloat16)
+    _need(pos, "pos", torch.int32, device=x.device)
+    T, H = x.shape
+    k = pos.shape[1]
+    if pos.shape[0] != T:
+        raise ValueError("pos must be [T, k]")
+    fp8 = dtype == "fp8"
+    if recv_x is None:
+        recv_x = torch.empty((num_recv_rows, H), dtype=torch.uint8 if fp8 else torch.bfloat16,
+                             device=x.device)
+    else:
+        _need(recv_x, "recv_x", torch.uint8 if fp8 else torch.bfloat16, (num_recv_rows, H), x.device)
+    if fp8 and recv_scales is None:
+        recv_scales = torch.empty((num_recv_rows, H // 128), dtype=torch.float32, device=x.device)
+    elif fp8:
+        _need(recv_scales, "recv_scales", torch.float32, (num_recv_rows, H // 128), x.device)
+    cfg = DispatchCfg(T, H, k, num_recv_rows, DISPATCH_DTYPES[dtype], units_per_wave)
+    _check(lib().moe_dispatch(ctypes.byref(cfg), _ptr(x), _ptr(pos), _ptr(recv_x),
+                              _ptr(recv_scales) if fp8 else None, _stream(x.device)))
+    return recv_x, (recv_scales if fp8 else None)
+
+
+def combine(y, pos, topk_w, out=None, units_per_wave: int = 0):
+    """y bf16 [N,H], pos int32 [T,k], topk_w fp32 [T,k] -> out bf16 [T,H]."""
+    torch = _torch()
+    _need(y, "y", torch.bfloat16)
+    _need(pos, "pos", torch.int32, device=y.device)
+    T, k = pos.shape
+    _need(topk_w, "topk_w", torch.float32, (T, k), y.device)
+    N, H = y.shape
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=y.device)
+    else:
+        _need(out, "out", torch.bfloat16, (T, H), y.device)
+    cfg = CombineCfg(T, H, k, N, units_per_wave)
+    _check(lib().moe_combine(ctypes.byref(cfg), _ptr(y), _ptr(pos), _ptr(topk_w), _ptr(out),
+                             _stream(y.device)))
+    return out
+
+
+def quantize_e4m3(x, out=None):
+    """fp32 tensor -> uint8 E4M3FN codes of the same shape."""
+    torch = _torch()
+    _need(x, "x", torch.float32)
+    if out is None:
+        out = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    else:
+        _need(out, "out", torch.uint8, x.shape, x.device)
+    _check(lib().moe_quantize_e4m3(_ptr(x), _ptr(out), x.numel(), _stream(x.device)))
+    return out
+
+
+__all__ = ["lib", "route_topk", "get_layout", "alloc_layout", "layout_workspace_bytes", "dispatch",
+           "combine", "quantize_e4m3", "Layout", "MoeError", "FLAG_CAPACITY_OVERFLOW", "FLAG_BAD_INDEX"]

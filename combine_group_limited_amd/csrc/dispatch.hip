@@ -1,0 +1,178 @@
+// dispatch.hip -- scatter each token into its k receive rows, FP8-quantised
+// with one scale per 128 channels (or verbatim BF16).
+//
+// Follows "Efficient and Portable Mixture-of-Experts Communication"
+// (Perplexity), section "Dispatch": tokens travel with their block scaling
+// factors and are unpacked into contiguous per-expert tensors for the grouped
+// GEMM; FP8 dispatch as in the DeepEP workloads ("DeepSeek, DeepEP
+// open-sourced", GeekNews 19421, "Performance > Normal kernels").
+//
+// Work unit: 512 channels of one token = one 16-byte load per lane of a wave
+// (lane l holds channels 8l .. 8l+7, so a wave load is 1 KiB contiguous).  A
+// 128-channel scale block is then exactly one 16-lane DPP row, and its absmax
+// is a 4-step row reduction of integer magnitudes (|bf16| bit patterns order
+// like their values).  A wave takes U consecutive units of one token, reads
+// them once, quantises them once, and writes the codes (8 bytes per lane, a
+// 512-byte contiguous store per unit) and the scales to each of the token's k
+// receive rows.  Every output byte is written by exactly one lane.
+#include "moe_device.hpp"
+#include "moe_internal.hpp"
+
+namespace cgl {
+namespace {
+
+constexpr int kUnit = 512;             // channels per wave-wide 16-byte load
+constexpr int kDispatchThreads = 256;  // four waves
+
+struct DispatchArgs {
+    const uint16_t* x;
+    const int32_t* pos;
+    void* recv_x;
+    float* recv_scales;
+    int T, H, k, N, S;
+    int units;   // ceil(H / 512)
+    int chunks;  // ceil(units / U): waves per token
+};
+
+__device__ __forceinline__ u32x4 load16(const uint16_t* p) {
+    return __builtin_nontemporal_load((const u32x4*)p);
+}
+
+// absmax of the 8 bf16 values held by a lane, as a 15-bit magnitude pattern
+__device__ __forceinline__ uint32_t lane_absmax_bits(const u32x4& v) {
+    const uint32_t m0 = max(v.x & 0x7FFFu, (v.x >> 16) & 0x7FFFu);
+    const uint32_t m1 = max(v.y & 0x7FFFu, (v.y >> 16) & 0x7FFFu);
+    const uint32_t m2 = max(v.z & 0x7FFFu, (v.z >> 16) & 0x7FFFu);
+    const uint32_t m3 = max(v.w & 0x7FFFu, (v.w >> 16) & 0x7FFFu);
+    return max(max(m0, m1), max(m2, m3));
+}
+
+template <int U>
+__global__ __launch_bounds__(kDispatchThreads) void dispatch_fp8_kernel(DispatchArgs a) {
+    const int lane = threadIdx.x & 63;
+    const int wave = blockIdx.x * (kDispatchThreads / kWave) + (threadIdx.x >> 6);
+    const int t = wave / a.chunks;
+    if (t >= a.T) return;  // wave-uniform
+    const int u0 = (wave - t * a.chunks) * U;
+    const uint16_t* xrow = a.x + (size_t)t * a.H;
+
+    u32x4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int c = (u0 + u) * kUnit + lane * 8;
+        v[u] = (c < a.H) ? load16(xrow + c) : u32x4{0u, 0u, 0u, 0u};
+    }
+
+    u32x2 code[U];
+    float scale[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const uint32_t m = row16_max_u32(lane_absmax_bits(v[u]));
+        const float amax = __uint_as_float(m << 16);
+        const float aa = amax > 0x1p-100f ? amax : 0x1p-100f;
+        scale[u] = aa / 448.0f;
+        const float inv = 448.0f / aa;
+        code[u].x = pack_e4m3x4(bf16_lo(v[u].x) * inv, bf16_hi(v[u].x) * inv, bf16_lo(v[u].y) * inv,
+                                bf16_hi(v[u].y) * inv);
+        code[u].y = pack_e4m3x4(bf16_lo(v[u].z) * inv, bf16_hi(v[u].z) * inv, bf16_lo(v[u].w) * inv,
+                                bf16_hi(v[u].w) * inv);
+    }
+
+    uint8_t* rx = (uint8_t*)a.recv_x;
+    const int32_t* prow = a.pos + (size_t)t * a.k;
+    for (int j = 0; j < a.k; ++j) {
+        const int p = prow[j];
+        if (p < 0 || p >= a.N) continue;  // dropped pair (wave-uniform)
+        uint8_t* dst = rx + (size_t)p * a.H;
+        float* sdst = a.recv_scales + (size_t)p * a.S;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int c = (u0 + u) * kUnit + lane * 8;
+            if (c < a.H) {
+                __builtin_nontemporal_store(code[u], (u32x2*)(dst + c));
+                if ((lane & 15) == 0) sdst[c >> 7] = scale[u];
+            }
+        }
+    }
+}
+
+template <int U>
+__global__ __launch_bounds__(kDispatchThreads) void dispatch_bf16_kernel(DispatchArgs a) {
+    const int lane = threadIdx.x & 63;
+    const int wave = blockIdx.x * (kDispatchThreads / kWave) + (threadIdx.x >> 6);
+    const int t = wave / a.chunks;
+    if (t >= a.T) return;
+    const int u0 = (wave - t * a.chunks) * U;
+    const uint16_t* xrow = a.x + (size_t)t * a.H;
+    u32x4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int c = (u0 + u) * kUnit + lane * 8;
+        v[u] = (c < a.H) ? load16(xrow + c) : u32x4{0u, 0u, 0u, 0u};
+    }
+    uint16_t* rx = (uint16_t*)a.recv_x;
+    const int32_t* prow = a.pos + (size_t)t * a.k;
+    for (int j = 0; j < a.k; ++j) {
+        const int p = prow[j];
+        if (p < 0 || p >= a.N) continue;
+        uint16_t* dst = rx + (size_t)p * a.H;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int c = (u0 + u) * kUnit + lane * 8;
+            if (c < a.H) __builtin_nontemporal_store(v[u], (u32x4*)(dst + c));
+        }
+    }
+}
+
+template <int U>
+hipError_t launch_u(DispatchArgs a, bool fp8, hipStream_t s) {
+    a.chunks = (a.units + U - 1) / U;
+    const long long waves = (long long)a.T * a.chunks;
+    const int wpb = kDispatchThreads / kWave;
+    const unsigned blocks = (unsigned)((waves + wpb - 1) / wpb);
+    if (fp8)
+        hipLaunchKernelGGL((dispatch_fp8_kernel<U>), dim3(blocks), dim3(kDispatchThreads), 0, s, a);
+    else
+        hipLaunchKernelGGL((dispatch_bf16_kernel<U>), dim3(blocks), dim3(kDispatchThreads), 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+int dispatch_units_per_wave(int T, int H) {
+    const int units = (H + kUnit - 1) / kUnit;
+    // enough waves to fill 256 CUs several times over, otherwise fewer loads
+    // per wave; U must divide the unit count to avoid idle lanes
+    static const int choices[] = {14, 8, 7, 4, 2, 1};
+    for (int u : choices) {
+        if (u > units || units % u) continue;
+        if ((long long)T * (units / u) >= 4096 || u == 1) return u;
+    }
+    return 1;
+}
+
+hipError_t launch_dispatch(const uint16_t* x, const int32_t* pos, void* recv_x, float* recv_scales, int T,
+                           int H, int k, int N, bool fp8, int upw, hipStream_t stream) {
+    DispatchArgs a{};
+    a.x = x;
+    a.pos = pos;
+    a.recv_x = recv_x;
+    a.recv_scales = recv_scales;
+    a.T = T;
+    a.H = H;
+    a.k = k;
+    a.N = N;
+    a.S = H / 128;
+    a.units = (H + kUnit - 1) / kUnit;
+    if (upw <= 0) upw = dispatch_units_per_wave(T, H);
+    switch (upw) {
+        case 14: return launch_u<14>(a, fp8, stream);
+        case 8: return launch_u<8>(a, fp8, stream);
+        case 7: return launch_u<7>(a, fp8, stream);
+        case 4: return launch_u<4>(a, fp8, stream);
+        case 2: return launch_u<2>(a, fp8, stream);
+        default: return launch_u<1>(a, fp8, stream);
+    }
+}
+
+}  // namespace cgl

@@ -1,0 +1,206 @@
+// moe_api.hip -- the C ABI declared in include/moe.h: argument validation on
+// the host, then kernel launches on the caller's stream.  No allocation, no
+// synchronisation, no state kept between calls (apart from the per-thread
+// error message).
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "moe.h"
+#include "moe_device.hpp"
+#include "moe_internal.hpp"
+
+namespace cgl {
+namespace {
+
+thread_local char g_err[512];
+
+moe_status fail(moe_status st, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+moe_status ok() {
+    g_err[0] = 0;
+    return MOE_OK;
+}
+
+moe_status hip_status(hipError_t e, const char* what) {
+    if (e == hipSuccess) return ok();
+    return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+__host__ __device__ inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+// out[i] = E4M3FN(in[i]); one thread converts four values (one 32-bit store).
+__global__ __launch_bounds__(256) void quantize_e4m3_kernel(const float* in, uint8_t* out, int64_t n) {
+    const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;  // quad index
+    const int64_t i = q * 4;
+    if (i + 3 < n) {
+        const uint32_t w = pack_e4m3x4(in[i], in[i + 1], in[i + 2], in[i + 3]);
+        if (aligned(out + i, 4)) {
+            *(uint32_t*)(out + i) = w;
+        } else {
+            for (int b = 0; b < 4; ++b) out[i + b] = (uint8_t)(w >> (8 * b));
+        }
+    } else if (i < n) {
+        float v[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        for (int64_t b = 0; i + b < n; ++b) v[b] = in[i + b];
+        const uint32_t w = pack_e4m3x4(v[0], v[1], v[2], v[3]);
+        for (int64_t b = 0; i + b < n; ++b) out[i + b] = (uint8_t)(w >> (8 * b));
+    }
+}
+
+}  // namespace
+
+hipError_t launch_quantize_e4m3(const float* in, uint8_t* out, int64_t n, hipStream_t stream) {
+    const int64_t quads = (n + 3) / 4;
+    const int64_t blocks = (quads + 255) / 256;
+    hipLaunchKernelGGL(quantize_e4m3_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, in, out, n);
+    return hipGetLastError();
+}
+
+}  // namespace cgl
+
+using namespace cgl;
+
+extern "C" {
+
+int32_t moe_abi_version(void) { return 1; }
+
+const char* moe_last_error(void) { return g_err; }
+
+const char* moe_status_string(moe_status s) {
+    switch (s) {
+        case MOE_OK: return "ok";
+        case MOE_ERR_INVALID: return "invalid argument";
+        case MOE_ERR_WORKSPACE: return "workspace too small";
+        case MOE_ERR_UNSUPPORTED: return "unsupported";
+        case MOE_ERR_HIP: return "HIP error";
+    }
+    return "unknown status";
+}
+
+moe_status moe_route_topk(const moe_route_cfg* c, const float* logits, int32_t* topk_idx, float* topk_w,
+                          void* stream) {
+    if (!c) return fail(MOE_ERR_INVALID, "route: cfg is NULL");
+    const int T = c->num_tokens, E = c->num_experts, G = c->num_groups, g = c->topk_group, k = c->topk;
+    if (T < 0) return fail(MOE_ERR_INVALID, "route: num_tokens %d < 0", T);
+    if (E < 1 || E > 512) return fail(MOE_ERR_INVALID, "route: num_experts %d outside [1, 512]", E);
+    if (G < 1 || G > 64 || E % G) return fail(MOE_ERR_INVALID, "route: num_groups %d must divide E and be <= 64", G);
+    if (g < 1 || g > G) return fail(MOE_ERR_INVALID, "route: topk_group %d outside [1, %d]", g, G);
+    const int Eg = E / G;
+    if (k < 1 || k > 64 || k > g * Eg)
+        return fail(MOE_ERR_INVALID, "route: topk %d outside [1, min(64, topk_group*E/G = %d)]", k, g * Eg);
+    int n = c->group_topn > 0 ? c->group_topn : k / g;
+    if (n < 1) n = 1;
+    if (c->group_topn < 0 || n > Eg)
+        return fail(MOE_ERR_INVALID, "route: group_topn %d outside [0, E/G = %d]", c->group_topn, Eg);
+    if (c->score_fn != MOE_SCORE_SIGMOID && c->score_fn != MOE_SCORE_SOFTMAX)
+        return fail(MOE_ERR_INVALID, "route: unknown score_fn %d", c->score_fn);
+    if (c->renormalize != 0 && c->renormalize != 1)
+        return fail(MOE_ERR_INVALID, "route: renormalize must be 0 or 1");
+    if (T == 0) return ok();
+    if (!logits || !topk_idx || !topk_w) return fail(MOE_ERR_INVALID, "route: NULL array");
+    if (!aligned(logits, 4) || !aligned(topk_idx, 4) || !aligned(topk_w, 4))
+        return fail(MOE_ERR_INVALID, "route: arrays must be 4-byte aligned");
+    return hip_status(launch_route(logits, topk_idx, topk_w, T, E, G, g, k, n, c->score_fn, c->renormalize,
+                                   (hipStream_t)stream),
+                      "route launch");
+}
+
+static moe_status check_layout_cfg(const moe_layout_cfg* c) {
+    if (!c) return fail(MOE_ERR_INVALID, "layout: cfg is NULL");
+    const int T = c->num_tokens, E = c->num_experts, k = c->topk, R = c->num_ranks, C = c->capacity;
+    if (T < 0) return fail(MOE_ERR_INVALID, "layout: num_tokens %d < 0", T);
+    if (E < 1 || E > 512) return fail(MOE_ERR_INVALID, "layout: num_experts %d outside [1, 512]", E);
+    if (k < 1 || k > 64) return fail(MOE_ERR_INVALID, "layout: topk %d outside [1, 64]", k);
+    if (R < 1 || R > E || E % R) return fail(MOE_ERR_INVALID, "layout: num_ranks %d must divide E", R);
+    if (C < 0) return fail(MOE_ERR_INVALID, "layout: capacity %d < 0", C);
+    if ((int64_t)T * k >= (1ll << 31)) return fail(MOE_ERR_INVALID, "layout: T*k too large");
+    if ((int64_t)E * C >= (1ll << 31)) return fail(MOE_ERR_INVALID, "layout: E*C too large");
+    return MOE_OK;
+}
+
+size_t moe_layout_workspace_bytes(const moe_layout_cfg* c) {
+    if (check_layout_cfg(c) != MOE_OK) return 0;
+    return layout_workspace_bytes(c->num_tokens, c->num_experts, c->num_ranks);
+}
+
+moe_status moe_get_layout(const moe_layout_cfg* c, const int32_t* topk_idx, int32_t* cnt_e, int32_t* cnt_r,
+                          int32_t* off_e, int32_t* off_r, int32_t* pos, int32_t* recv_src, int32_t* flags,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+    moe_status st = check_layout_cfg(c);
+    if (st != MOE_OK) return st;
+    const int T = c->num_tokens;
+    if (!cnt_e || !cnt_r || !off_e || !off_r || !flags)
+        return fail(MOE_ERR_INVALID, "layout: NULL output array");
+    if (T > 0 && (!topk_idx || !pos)) return fail(MOE_ERR_INVALID, "layout: NULL topk_idx or pos");
+    const int64_t N = c->capacity > 0 ? (int64_t)c->num_experts * c->capacity : (int64_t)T * c->topk;
+    if (N > 0 && !recv_src) return fail(MOE_ERR_INVALID, "layout: NULL recv_src");
+    const void* ptrs[] = {topk_idx, cnt_e, cnt_r, off_e, off_r, pos, recv_src, flags};
+    for (const void* p : ptrs)
+        if (!aligned(p, 4)) return fail(MOE_ERR_INVALID, "layout: arrays must be 4-byte aligned");
+    const size_t need = layout_workspace_bytes(T, c->num_experts, c->num_ranks);
+    if (!workspace || workspace_bytes < need)
+        return fail(MOE_ERR_WORKSPACE, "layout: workspace needs %zu bytes, got %zu", need,
+                    workspace ? workspace_bytes : (size_t)0);
+    if (!aligned(workspace, 4)) return fail(MOE_ERR_INVALID, "layout: workspace must be 4-byte aligned");
+    return hip_status(launch_layout(topk_idx, cnt_e, cnt_r, off_e, off_r, pos, recv_src, flags, workspace, T,
+                                    c->num_experts, c->topk, c->num_ranks, c->capacity, (hipStream_t)stream),
+                      "layout launch");
+}
+
+moe_status moe_dispatch(const moe_dispatch_cfg* c, const uint16_t* x, const int32_t* pos, void* recv_x,
+                        float* recv_scales, void* stream) {
+    if (!c) return fail(MOE_ERR_INVALID, "dispatch: cfg is NULL");
+    const int T = c->num_tokens, H = c->hidden, k = c->topk, N = c->num_recv_rows;
+    if (T < 0 || N < 0) return fail(MOE_ERR_INVALID, "dispatch: negative size");
+    if (k < 1 || k > 64) return fail(MOE_ERR_INVALID, "dispatch: topk %d outside [1, 64]", k);
+    const bool fp8 = c->dtype == MOE_DISPATCH_FP8_E4M3;
+    if (!fp8 && c->dtype != MOE_DISPATCH_BF16) return fail(MOE_ERR_INVALID, "dispatch: unknown dtype %d", c->dtype);
+    if (H < 1 || (fp8 && H % 128) || (!fp8 && H % 8))
+        return fail(MOE_ERR_INVALID, "dispatch: hidden %d must be a positive multiple of %d", H, fp8 ? 128 : 8);
+    const int upw = c->units_per_wave;
+    if (!(upw == 0 || upw == 1 || upw == 2 || upw == 4 || upw == 7 || upw == 8 || upw == 14))
+        return fail(MOE_ERR_INVALID, "dispatch: units_per_wave %d not in {0,1,2,4,7,8,14}", upw);
+    if (T == 0) return ok();
+    if (!x || !pos || (N > 0 && !recv_x) || (fp8 && N > 0 && !recv_scales))
+        return fail(MOE_ERR_INVALID, "dispatch: NULL array");
+    if (!aligned(x, 16) || !aligned(recv_x, 16) || !aligned(pos, 4) || !aligned(recv_scales, 4))
+        return fail(MOE_ERR_INVALID, "dispatch: x/recv_x must be 16-byte aligned, pos/scales 4-byte");
+    if (N == 0) return ok();
+    return hip_status(launch_dispatch(x, pos, recv_x, recv_scales, T, H, k, N, fp8, upw, (hipStream_t)stream),
+                      "dispatch launch");
+}
+
+moe_status moe_combine(const moe_combine_cfg* c, const uint16_t* y, const int32_t* pos, const float* topk_w,
+                       uint16_t* out, void* stream) {
+    if (!c) return fail(MOE_ERR_INVALID, "combine: cfg is NULL");
+    const int T = c->num_tokens, H = c->hidden, k = c->topk, N = c->num_recv_rows;
+    if (T < 0 || N < 0) return fail(MOE_ERR_INVALID, "combine: negative size");
+    if (k < 1 || k > 64) return fail(MOE_ERR_INVALID, "combine: topk %d outside [1, 64]", k);
+    if (H < 1 || H % 8) return fail(MOE_ERR_INVALID, "combine: hidden %d must be a positive multiple of 8", H);
+    const int upw = c->units_per_wave;
+    if (!(upw == 0 || upw == 1 || upw == 2 || upw == 4 || upw == 7))
+        return fail(MOE_ERR_INVALID, "combine: units_per_wave %d not in {0,1,2,4,7}", upw);
+    if (T == 0) return ok();
+    if (!pos || !topk_w || !out || (N > 0 && !y)) return fail(MOE_ERR_INVALID, "combine: NULL array");
+    if (!aligned(y, 16) || !aligned(out, 16) || !aligned(pos, 4) || !aligned(topk_w, 4))
+        return fail(MOE_ERR_INVALID, "combine: y/out must be 16-byte aligned, pos/w 4-byte");
+    return hip_status(launch_combine(y, pos, topk_w, out, T, H, k, N, upw, (hipStream_t)stream),
+                      "combine launch");
+}
+
+moe_status moe_quantize_e4m3(const float* in, uint8_t* out, int64_t n, void* stream) {
+    if (n < 0) return fail(MOE_ERR_INVALID, "quantize: n < 0");
+    if (n == 0) return ok();
+    if (!in || !out) return fail(MOE_ERR_INVALID, "quantize: NULL array");
+    if (!aligned(in, 4)) return fail(MOE_ERR_INVALID, "quantize: input must be 4-byte aligned");
+    if ((n + 3) / 4 / 256 >= (1ll << 31)) return fail(MOE_ERR_INVALID, "quantize: n too large");
+    return hip_status(launch_quantize_e4m3(in, out, n, (hipStream_t)stream), "quantize launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,162 @@
+// moe_device.hpp -- device-side helpers shared by the gfx950 kernels.
+//
+// Wave64 throughout: every helper that exchanges data between lanes assumes a
+// full 64-lane wave with all lanes active.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace cgl {
+
+constexpr int kWave = 64;
+
+// Native vector types (usable with the nontemporal load/store builtins).
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------------------
+// fp32 exponential used for router scores.  Router selection must agree bit
+// for bit with an independent host implementation, so the recipe is fixed:
+//   clamp: z >= 80 -> +inf, z <= -80 -> 0 (keeps every result a normal number)
+//   n = rint(z * log2(e));  r = z - n*ln2_hi - n*ln2_lo (two fmas; ln2_hi has
+//   17 significant bits so n*ln2_hi is exact)
+//   p = sum_{i<=7} r^i/i! by Horner with fma, coefficients rounded to fp32
+//   result = p * 2^n (exact, v_ldexp_f32)
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float exp_fixed(float z) {
+    if (z >= 80.0f) return __builtin_inff();
+    if (z <= -80.0f) return 0.0f;
+    const float n = __builtin_rintf(z * 1.44269504f);
+    float r = __builtin_fmaf(-n, 0x1.62e4p-1f, z);
+    r = __builtin_fmaf(-n, 1.4286068e-6f, r);
+    float p = 0x1.a01a02p-13f;                 // 1/5040
+    p = __builtin_fmaf(p, r, 0x1.6c16c2p-10f); // 1/720
+    p = __builtin_fmaf(p, r, 0x1.111112p-7f);  // 1/120
+    p = __builtin_fmaf(p, r, 0x1.555556p-5f);  // 1/24
+    p = __builtin_fmaf(p, r, 0x1.555556p-3f);  // 1/6
+    p = __builtin_fmaf(p, r, 0.5f);
+    p = __builtin_fmaf(p, r, 1.0f);
+    p = __builtin_fmaf(p, r, 1.0f);
+    return __builtin_ldexpf(p, (int)n);
+}
+
+__device__ __forceinline__ float sigmoid_fixed(float x) {
+    const float e = exp_fixed(-x);
+    return 1.0f / (1.0f + e);  // IEEE division (no fast-math in this build)
+}
+
+// ---------------------------------------------------------------------------
+// Ordering keys: larger key = ranks first.  High word: the score's fp32 bits
+// mapped to an unsigned order (-0 folded onto +0 so they compare equal); low
+// word: ~index so that among equal scores the lower index wins.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t float_order(float v) {
+    uint32_t b = __float_as_uint(v + 0.0f);          // -0 + 0 = +0
+    return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+__device__ __forceinline__ float order_float(uint32_t o) {
+    return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
+}
+
+__device__ __forceinline__ uint64_t make_key(float v, uint32_t index) {
+    return ((uint64_t)float_order(v) << 32) | (uint64_t)(0xFFFFFFFFu - index);
+}
+
+__device__ __forceinline__ uint32_t key_index(uint64_t k) {
+    return 0xFFFFFFFFu - (uint32_t)k;
+}
+
+__device__ __forceinline__ float key_value(uint64_t k) {
+    return order_float((uint32_t)(k >> 32));
+}
+
+__device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+
+// DPP lane exchange of a 32-bit value within rows of 16 lanes.
+//   0xB1 quad_perm[1,0,3,2] (lane ^ 1)    0x4E quad_perm[2,3,0,1] (lane ^ 2)
+//   0x141 row_half_mirror (i <-> 7-i)     0x140 row_mirror (i <-> 15-i)
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp32(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp64(uint64_t v) {
+    const uint32_t lo = dpp32<CTRL>((uint32_t)v);
+    const uint32_t hi = dpp32<CTRL>((uint32_t)(v >> 32));
+    return ((uint64_t)hi << 32) | lo;
+}
+
+__device__ __forceinline__ uint32_t bperm32(uint32_t v, int src_lane) {
+    return (uint32_t)__builtin_amdgcn_ds_bpermute(src_lane << 2, (int)v);
+}
+
+__device__ __forceinline__ uint64_t bperm64(uint64_t v, int src_lane) {
+    return ((uint64_t)bperm32((uint32_t)(v >> 32), src_lane) << 32) | bperm32((uint32_t)v, src_lane);
+}
+
+// Max over aligned segments of W lanes (W a power of two <= 64); every lane of
+// a segment receives the segment's maximum.  Within a row (W <= 16) each step
+// pairs every lane with a lane of the other half of its current sub-segment.
+template <int W>
+__device__ __forceinline__ uint64_t seg_max64(uint64_t v) {
+    if constexpr (W >= 2) v = umax64(v, dpp64<0xB1>(v));
+    if constexpr (W >= 4) v = umax64(v, dpp64<0x4E>(v));
+    if constexpr (W >= 8) v = umax64(v, dpp64<0x141>(v));
+    if constexpr (W >= 16) v = umax64(v, dpp64<0x140>(v));
+    const int lane = (int)__lane_id();
+    if constexpr (W >= 32) v = umax64(v, bperm64(v, lane ^ 16));
+    if constexpr (W >= 64) v = umax64(v, bperm64(v, lane ^ 32));
+    return v;
+}
+
+// Max over the whole wave, returned as a wave-uniform value.
+__device__ __forceinline__ uint64_t wave_max64(uint64_t v) {
+    v = seg_max64<16>(v);
+    const uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
+    uint64_t r = 0;
+#pragma unroll
+    for (int row = 0; row < 4; ++row) {
+        const uint64_t rv = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)hi, row * 16) << 32) |
+                            (uint32_t)__builtin_amdgcn_readlane((int)lo, row * 16);
+        r = umax64(r, rv);
+    }
+    return r;
+}
+
+// Max of non-negative 32-bit values over each row of 16 lanes (all lanes of
+// the row receive it).
+__device__ __forceinline__ uint32_t row16_max_u32(uint32_t v) {
+    v = max(v, dpp32<0xB1>(v));
+    v = max(v, dpp32<0x4E>(v));
+    v = max(v, dpp32<0x141>(v));
+    v = max(v, dpp32<0x140>(v));
+    return v;
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// Two fp32 -> two bf16 (round to nearest even), packed lo | hi << 16.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    const __bf16 a = (__bf16)lo;
+    const __bf16 b = (__bf16)hi;
+    return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+
+// Four fp32 -> four OCP E4M3FN codes (round to nearest even), byte i = input i.
+// Inputs are first clamped to [-448, 448] so magnitudes above the largest
+// finite code saturate instead of becoming NaN; the clamp keeps -0.
+__device__ __forceinline__ uint32_t pack_e4m3x4(float a, float b, float c, float d) {
+    a = __builtin_amdgcn_fmed3f(a, -448.0f, 448.0f);
+    b = __builtin_amdgcn_fmed3f(b, -448.0f, 448.0f);
+    c = __builtin_amdgcn_fmed3f(c, -448.0f, 448.0f);
+    d = __builtin_amdgcn_fmed3f(d, -448.0f, 448.0f);
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+    return (uint32_t)w;
+}
+
+}  // namespace cgl

@@ -1,0 +1,30 @@
+// moe_internal.hpp -- launchers behind the C ABI (host side).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace cgl {
+
+hipError_t launch_route(const float* logits, int32_t* idx, float* w, int T, int E, int G, int g, int k,
+                        int n, int score_fn, int renorm, hipStream_t stream);
+
+size_t layout_workspace_bytes(int T, int E, int R);
+size_t layout_lds_bytes_host(int E, int R);
+hipError_t launch_layout(const int32_t* idx, int32_t* cnt_e, int32_t* cnt_r, int32_t* off_e, int32_t* off_r,
+                         int32_t* pos, int32_t* recv_src, int32_t* flags, void* workspace, int T, int E,
+                         int k, int R, int C, hipStream_t stream);
+
+// upw: 512-channel units per wave (0 = the library's choice for the shape)
+int dispatch_units_per_wave(int T, int H);
+hipError_t launch_dispatch(const uint16_t* x, const int32_t* pos, void* recv_x, float* recv_scales, int T,
+                           int H, int k, int N, bool fp8, int upw, hipStream_t stream);
+
+int combine_units_per_wave(int T, int H);
+hipError_t launch_combine(const uint16_t* y, const int32_t* pos, const float* w, uint16_t* out, int T, int H,
+                          int k, int N, int upw, hipStream_t stream);
+
+hipError_t launch_quantize_e4m3(const float* in, uint8_t* out, int64_t n, hipStream_t stream);
+
+}  // namespace cgl

@@ -1,0 +1,234 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) MoE dispatch/combine library.
+ *
+ * The library runs, on one GPU, one rank's share of the token exchange of a
+ * Mixture-of-Experts layer, in four calls that follow the pages' statement of
+ * the problem:
+ *
+ *   moe_route_topk  router scores -> group-limited top-k experts and weights
+ *   moe_get_layout  per-expert / per-rank counts, offsets, and every
+ *                   (token, slot) pair's receive row (the "handle")
+ *   moe_dispatch    copy each token into its k receive rows of an
+ *                   expert-contiguous buffer, FP8-quantised with per-128-
+ *                   channel scales (or verbatim BF16)
+ *   moe_combine     out[t] = sum_j w[t,j] * y[pos[t,j]]  (BF16 in and out)
+ *
+ * Conventions for every call:
+ *   - All array pointers are DEVICE pointers owned by the caller; arrays are
+ *     dense and row-major.  bf16 values are passed as uint16_t bit patterns.
+ *   - The library never allocates or frees memory in these calls and keeps no
+ *     state between them.
+ *   - Every call is asynchronous: it validates its arguments on the host,
+ *     enqueues kernels on `stream` (a hipStream_t; NULL = the null stream)
+ *     and returns without synchronising.
+ *   - Host-side validation failures return MOE_ERR_INVALID and enqueue nothing.
+ *     Launch failures return MOE_ERR_HIP.  moe_last_error() then describes the
+ *     failure (per thread).
+ *   - num_tokens == 0 is valid: route, dispatch and combine do nothing;
+ *     moe_get_layout writes zero counts and offsets (and -1 to every padded
+ *     recv_src row).
+ *   - Pointers to 16-bit and FP8 row data must be 16-byte aligned.
+ *   - Device-side data that is out of range (an expert index outside [0,E), a
+ *     receive row outside [0,N)) never causes an out-of-bounds access: the
+ *     offending pair is skipped and, in moe_get_layout, reported in *flags.
+ *   - Results are deterministic: every output element is written by exactly
+ *     one lane and no global atomics take part in any result.
+ */
+#ifndef CGL_MOE_H
+#define CGL_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_ERR_INVALID = 1,     /* bad shape, null pointer, or inconsistent sizes */
+    MOE_ERR_WORKSPACE = 2,   /* workspace missing or smaller than required */
+    MOE_ERR_UNSUPPORTED = 4, /* valid request this build does not implement */
+    MOE_ERR_HIP = 5          /* a HIP runtime call or kernel launch failed */
+} moe_status;
+
+typedef enum { MOE_SCORE_SIGMOID = 0, MOE_SCORE_SOFTMAX = 1 } moe_score_fn;
+typedef enum { MOE_DISPATCH_FP8_E4M3 = 0, MOE_DISPATCH_BF16 = 1 } moe_dispatch_dtype;
+
+/* Bits of the *flags word written by moe_get_layout. */
+#define MOE_FLAG_CAPACITY_OVERFLOW 1  /* padded mode: some expert got more than C pairs */
+#define MOE_FLAG_BAD_INDEX 2          /* an index outside [0,E) or repeated in a token */
+
+/* ------------------------------------------------------------------------ */
+/* moe_route_topk -- group-limited top-k gating.                            */
+/*                                                                          */
+/* Follows "Efficient and Portable Mixture-of-Experts Communication"        */
+/* (Perplexity), section "Introduction": the router gives each token a      */
+/* score distribution over experts, the token goes to its top-K experts and */
+/* the outputs are summed with the router weights; and "DeepSeek, DeepEP    */
+/* open-sourced" (GeekNews 19421), topic body and "Performance > Normal     */
+/* kernels": group-limited gating, top-4 groups then top-8 experts.         */
+/*                                                                          */
+/* For each token t (logits row l = logits[t, 0..E-1]):                     */
+/*  1. score s_e = 1/(1+exp(-l_e)) (SIGMOID) or s_e = l_e (SOFTMAX: softmax */
+/*     is increasing, so selection on the logits is selection on the        */
+/*     probabilities);                                                      */
+/*  2. if num_groups G > 1: group gamma (experts gamma*E/G .. +E/G-1) scores */
+/*     the sum of its group_topn largest s_e (0 = topk/topk_group, at least */
+/*     1), added in descending order; keep the topk_group best groups;      */
+/*  3. take the topk best experts of the kept groups, slots in descending   */
+/*     score; equal scores go to the lower index (-0 equals +0);            */
+/*  4. weights: renormalize=1: SIGMOID w_j = s_j / (s_0+...+s_{k-1}),       */
+/*     SOFTMAX w_j = exp(l_j - l_0) / sum_i exp(l_i - l_0); renormalize=0:  */
+/*     SIGMOID w_j = s_j, SOFTMAX w_j = full softmax probability.           */
+/*  exp is a fixed fp32 recipe (Cody-Waite reduction by ln 2, degree-7      */
+/*  Taylor polynomial by fma, exact 2^n scaling, clamped at |z| >= 80), so   */
+/*  indices and weights are reproducible bit for bit.                       */
+/*                                                                          */
+/* logits   fp32  [T, E]   in                                               */
+/* topk_idx int32 [T, k]   out, expert ids                                  */
+/* topk_w   fp32  [T, k]   out, weights                                     */
+/* Limits: 1 <= E <= 512, 1 <= G <= 64, E % G == 0, 1 <= topk_group <= G,  */
+/*         1 <= k <= min(64, topk_group*E/G), 0 <= group_topn <= E/G.       */
+/* ------------------------------------------------------------------------ */
+typedef struct {
+    int32_t num_tokens;   /* T */
+    int32_t num_experts;  /* E */
+    int32_t num_groups;   /* G (1 = no group limit) */
+    int32_t topk_group;   /* groups kept per token */
+    int32_t topk;         /* k */
+    int32_t group_topn;   /* experts summed per group score; 0 = topk/topk_group */
+    int32_t score_fn;     /* moe_score_fn */
+    int32_t renormalize;  /* 0 or 1 */
+} moe_route_cfg;
+
+moe_status moe_route_topk(const moe_route_cfg* cfg, const float* logits, int32_t* topk_idx,
+                          float* topk_w, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* moe_get_layout -- routing layout (the dispatch "handle").                */
+/*                                                                          */
+/* Follows the Perplexity page, sections "Portable kernels" (a fixed        */
+/* per-expert capacity lets every sender derive a unique destination        */
+/* address with no synchronisation) and "Dispatch" (per-expert token counts;*/
+/* the receiver keeps source, expert and token index for the combine), and  */
+/* the DeepEP V2 digest, section "training/prefill/decoding usage" (the     */
+/* handle carries the per-expert token counts for the grouped GEMM).        */
+/*                                                                          */
+/* A stable counting sort of the T*k (token, slot) pairs by expert:         */
+/*   cnt_e[e]   = #pairs routed to e                         int32 [E]      */
+/*   cnt_r[r]   = #tokens with >= 1 expert on virtual rank r int32 [R]      */
+/*                (rank r owns experts r*E/R .. r*E/R + E/R - 1)            */
+/*   off_e[e]   = cnt_e[0] + ... + cnt_e[e-1]                int32 [E+1]    */
+/*   off_r[r]   = off_e[r*E/R]  (pairs before rank r)        int32 [R+1]    */
+/*   pos[t,j]   = receive row of pair (t,j)                  int32 [T,k]    */
+/*       compact (capacity 0): off_e[e] + #{t' < t routed to e}; N = T*k    */
+/*       padded  (capacity C): e*C + #{t' < t routed to e}, or -1 when that */
+/*                is >= C (dropped; MOE_FLAG_CAPACITY_OVERFLOW); N = E*C    */
+/*   recv_src[p] = t*k + j for p = pos[t,j]; -1 for empty padded rows       */
+/*                                                           int32 [N]      */
+/*   flags[0]   = MOE_FLAG_* bits (0 = all good)             int32 [1]      */
+/* Counts are never clamped.  If MOE_FLAG_BAD_INDEX is set the other        */
+/* outputs are unspecified (but every write stays in bounds).               */
+/* workspace: device memory of at least moe_layout_workspace_bytes(cfg).    */
+/* Limits: 1 <= E <= 512, 1 <= k <= 64, 1 <= R <= E, E % R == 0,          */
+/*         T*k < 2^31, E*C < 2^31.                                          */
+/* ------------------------------------------------------------------------ */
+typedef struct {
+    int32_t num_tokens;   /* T */
+    int32_t num_experts;  /* E */
+    int32_t topk;         /* k */
+    int32_t num_ranks;    /* R */
+    int32_t capacity;     /* 0 = compact; C > 0 = padded slots per expert */
+} moe_layout_cfg;
+
+size_t moe_layout_workspace_bytes(const moe_layout_cfg* cfg);
+
+moe_status moe_get_layout(const moe_layout_cfg* cfg, const int32_t* topk_idx, int32_t* cnt_e,
+                          int32_t* cnt_r, int32_t* off_e, int32_t* off_r, int32_t* pos,
+                          int32_t* recv_src, int32_t* flags, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* moe_dispatch -- scatter tokens into the expert-contiguous receive buffer. */
+/*                                                                          */
+/* Follows the Perplexity page, section "Dispatch": tokens are sent with    */
+/* their block scaling factors and land in contiguous per-expert tensors    */
+/* for the grouped GEMM; FP8 dispatch as in the DeepEP performance          */
+/* workloads (GeekNews 19421, "Performance > Normal kernels").              */
+/*                                                                          */
+/* For every pair (t,j) with p = pos[t,j] in [0, N):                        */
+/*  FP8_E4M3: for each block b of 128 channels, a = max(max_i |x[t,i]|,     */
+/*    2^-100), scale = a/448, inv = 448/a (fp32, correctly rounded),        */
+/*    recv_x[p, 128b+i] = E4M3FN nearest-even of the fp32 product           */
+/*    x[t,128b+i]*inv (OCP E4M3FN: max 448, sign kept), recv_scales[p,b] =  */
+/*    scale.  Dequantise as code * scale.                                    */
+/*  BF16: recv_x[p, :] = x[t, :] bit for bit.                               */
+/* Rows no pair addresses are not written.  pos of -1 (dropped) is skipped. */
+/*                                                                          */
+/* x           bf16 [T, H]                in                                */
+/* pos         int32 [T, k]               in (from moe_get_layout)          */
+/* recv_x      uint8 [N, H] (FP8) or bf16 [N, H]                 out        */
+/* recv_scales fp32 [N, H/128] (FP8; NULL for BF16)               out        */
+/* Limits: H % 128 == 0 (FP8) or H % 8 == 0 (BF16); 1 <= k <= 64.           */
+/* ------------------------------------------------------------------------ */
+typedef struct {
+    int32_t num_tokens;     /* T */
+    int32_t hidden;         /* H */
+    int32_t topk;           /* k */
+    int32_t num_recv_rows;  /* N */
+    int32_t dtype;          /* moe_dispatch_dtype */
+    int32_t units_per_wave; /* launch-shape override, 512-channel units per wave
+                               (1, 2, 4, 7, 8 or 14); 0 = library choice.  Like
+                               the num_sms override of the DeepEP V2 digest,
+                               section "ElasticBuffer interface", it changes
+                               speed only, never results. */
+} moe_dispatch_cfg;
+
+moe_status moe_dispatch(const moe_dispatch_cfg* cfg, const uint16_t* x, const int32_t* pos,
+                        void* recv_x, float* recv_scales, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* moe_combine -- top-k weighted gather-reduce back into token order.       */
+/*                                                                          */
+/* Follows the Perplexity page, section "Combine": the receiver reads each  */
+/* expert's 16-bit output for the token, picks buffer and weight from the   */
+/* routing table, forms the weighted sum and writes it to a caller-         */
+/* allocated tensor.                                                        */
+/*                                                                          */
+/* out[t, c] = bf16_rne( fma chain over j = 0..k-1 of w[t,j] * y[pos[t,j],c]*/
+/*             in fp32, starting from 0 );  pairs with pos outside [0, N)    */
+/*             contribute nothing.                                          */
+/* y      bf16 [N, H]   in (expert outputs, rows in receive order)          */
+/* pos    int32 [T, k]  in                                                  */
+/* topk_w fp32 [T, k]   in                                                  */
+/* out    bf16 [T, H]   out (must not alias y)                              */
+/* Limits: H % 8 == 0; 1 <= k <= 64.                                        */
+/* ------------------------------------------------------------------------ */
+typedef struct {
+    int32_t num_tokens;     /* T */
+    int32_t hidden;         /* H */
+    int32_t topk;           /* k */
+    int32_t num_recv_rows;  /* N */
+    int32_t units_per_wave; /* launch-shape override (1, 2, 4 or 7); 0 = library choice */
+} moe_combine_cfg;
+
+moe_status moe_combine(const moe_combine_cfg* cfg, const uint16_t* y, const int32_t* pos,
+                       const float* topk_w, uint16_t* out, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* moe_quantize_e4m3 -- the element conversion moe_dispatch uses, exposed   */
+/* on its own: out[i] = E4M3FN nearest-even of in[i], magnitudes above 448  */
+/* saturate to 448, sign kept (codes for NaN inputs are unspecified).       */
+/* in fp32 [n], out uint8 [n]; n >= 0.                                      */
+/* ------------------------------------------------------------------------ */
+moe_status moe_quantize_e4m3(const float* in, uint8_t* out, int64_t n, void* stream);
+
+const char* moe_status_string(moe_status status);
+const char* moe_last_error(void);
+int32_t moe_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CGL_MOE_H */

@@ -1,0 +1,136 @@
+"""The C ABI on the host: the library loads, exports every function that
+include/moe.h declares, and rejects bad arguments before touching a GPU.
+No kernel is launched here."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import combine_group_limited_amd as moe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    names = declared_functions()
+    assert {"moe_route_topk", "moe_get_layout", "moe_dispatch", "moe_combine"} <= set(names)
+    L = moe.lib()
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_no_undefined_symbols_beyond_runtime():
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", moe.LIB_PATH], capture_output=True,
+                         text=True).stdout
+    exported = set(re.findall(r" T (moe_[a-z0-9_]+)", out))
+    assert exported == set(declared_functions())
+
+
+def test_status_strings_and_version():
+    L = moe.lib()
+    assert L.moe_abi_version() == 1
+    for s in (0, 1, 2, 4, 5):
+        assert L.moe_status_string(s)
+
+
+def _route(cfg_vals, logits=None, idx=None, w=None):
+    L = moe.lib()
+    cfg = moe.RouteCfg(*cfg_vals)
+    return L.moe_route_topk(ctypes.byref(cfg), logits, idx, w, None)
+
+
+@pytest.mark.parametrize("vals", [
+    (-1, 256, 8, 4, 8, 0, 0, 1),      # negative T
+    (4, 0, 1, 1, 1, 0, 0, 1),         # no experts
+    (4, 1024, 8, 4, 8, 0, 0, 1),      # E above the limit
+    (4, 256, 7, 4, 8, 0, 0, 1),       # G does not divide E
+    (4, 256, 8, 9, 8, 0, 0, 1),       # g > G
+    (4, 256, 8, 0, 8, 0, 0, 1),       # g = 0
+    (4, 256, 8, 1, 33, 0, 0, 1),      # k > g*E/G
+    (4, 256, 8, 4, 8, 33, 0, 1),      # group_topn > E/G
+    (4, 256, 8, 4, 8, -1, 0, 1),      # negative group_topn
+    (4, 256, 8, 4, 8, 0, 2, 1),       # unknown score fn
+    (4, 256, 8, 4, 8, 0, 0, 3),       # renormalize not 0/1
+    (4, 512, 128, 4, 8, 0, 0, 1),     # more than 64 groups
+    (4, 256, 8, 4, 8, 0, 0, 1),       # valid shape, NULL arrays
+])
+def test_route_rejects(vals):
+    assert _route(vals) == moe.MOE_ERR_INVALID
+    assert moe.lib().moe_last_error()
+
+
+def test_route_zero_tokens_is_noop():
+    assert _route((0, 256, 8, 4, 8, 0, 0, 1)) == moe.MOE_OK
+
+
+def test_layout_workspace_and_rejects():
+    L = moe.lib()
+    ok = moe.LayoutCfg(4096, 256, 8, 32, 0)
+    assert L.moe_layout_workspace_bytes(ctypes.byref(ok)) >= 4 * 16 * (256 + 32 + 1)
+    for vals in [(4, 256, 8, 33, 0), (4, 256, 0, 32, 0), (4, 256, 8, 32, -1), (-1, 256, 8, 32, 0),
+                 (4, 600, 8, 8, 0), (4, 256, 8, 512, 0)]:
+        cfg = moe.LayoutCfg(*vals)
+        assert L.moe_layout_workspace_bytes(ctypes.byref(cfg)) == 0
+        st = L.moe_get_layout(ctypes.byref(cfg), *([None] * 9), 0, None)
+        assert st == moe.MOE_ERR_INVALID
+    # valid shape: missing arrays, then missing workspace
+    st = L.moe_get_layout(ctypes.byref(ok), *([None] * 9), 0, None)
+    assert st == moe.MOE_ERR_INVALID
+    fake = ctypes.c_void_p(1 << 20)  # never dereferenced: validation fails first
+    args = [fake] * 8
+    st = L.moe_get_layout(ctypes.byref(ok), *args, None, 0, None)
+    assert st == moe.MOE_ERR_WORKSPACE
+    st = L.moe_get_layout(ctypes.byref(ok), *args, fake, 16, None)
+    assert st == moe.MOE_ERR_WORKSPACE
+
+
+def test_dispatch_rejects():
+    L = moe.lib()
+    fake = ctypes.c_void_p(1 << 20)
+    for vals in [(4, 7168, 0, 32, 0, 0), (4, 100, 8, 32, 0, 0), (4, 7168, 8, 32, 3, 0),
+                 (4, 12, 8, 32, 1, 0), (4, 7168, 8, 32, 0, 5), (-1, 7168, 8, 32, 0, 0)]:
+        cfg = moe.DispatchCfg(*vals)
+        assert L.moe_dispatch(ctypes.byref(cfg), fake, fake, fake, fake, None) == moe.MOE_ERR_INVALID
+    cfg = moe.DispatchCfg(4, 7168, 8, 32, 0, 0)
+    assert L.moe_dispatch(ctypes.byref(cfg), None, fake, fake, fake, None) == moe.MOE_ERR_INVALID
+    assert L.moe_dispatch(ctypes.byref(cfg), fake, fake, fake, None, None) == moe.MOE_ERR_INVALID
+    mis = ctypes.c_void_p((1 << 20) + 8)   # not 16-byte aligned
+    assert L.moe_dispatch(ctypes.byref(cfg), mis, fake, fake, fake, None) == moe.MOE_ERR_INVALID
+    zero = moe.DispatchCfg(0, 7168, 8, 0, 0, 0)
+    assert L.moe_dispatch(ctypes.byref(zero), None, None, None, None, None) == moe.MOE_OK
+
+
+def test_combine_rejects():
+    L = moe.lib()
+    fake = ctypes.c_void_p(1 << 20)
+    for vals in [(4, 7168, 0, 32, 0), (4, 7, 8, 32, 0), (4, 7168, 8, 32, 3), (4, 7168, 65, 32, 0)]:
+        cfg = moe.CombineCfg(*vals)
+        assert L.moe_combine(ctypes.byref(cfg), fake, fake, fake, fake, None) == moe.MOE_ERR_INVALID
+    cfg = moe.CombineCfg(4, 7168, 8, 32, 0)
+    assert L.moe_combine(ctypes.byref(cfg), fake, fake, None, fake, None) == moe.MOE_ERR_INVALID
+    zero = moe.CombineCfg(0, 7168, 8, 0, 0)
+    assert L.moe_combine(ctypes.byref(zero), None, None, None, None, None) == moe.MOE_OK
+
+
+def test_quantize_rejects():
+    L = moe.lib()
+    assert L.moe_quantize_e4m3(None, None, -1, None) == moe.MOE_ERR_INVALID
+    assert L.moe_quantize_e4m3(None, None, 0, None) == moe.MOE_OK
+    assert L.moe_quantize_e4m3(None, None, 10, None) == moe.MOE_ERR_INVALID
+
+
+def test_binding_has_no_fallback(tmp_path, monkeypatch):
+    """Without the built library the binding raises; it never computes on the CPU."""
+    monkeypatch.setattr(moe, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(moe, "_lib", None)
+    with pytest.raises(ImportError):
+        moe.lib()
