@@ -8,16 +8,17 @@
 // and the DeepEP V2 digest, section "training/prefill/decoding usage"
 // (per-expert token counts for the grouped GEMM).
 //
-// Tokens are cut into blocks of 256 (four waves of 64).  In a block, each
-// wave builds one 64-bit lane mask per expert (and per rank) in LDS with
-// ds_or_b64; popcounts give the per-block counts, and a token's rank among
-// the earlier tokens of its expert is
+// Tokens are cut into blocks of 256 (four waves of 64, one token per lane).
+// Each wave builds one 64-bit lane mask per expert (and per rank) in LDS with
+// ds_or_b64; popcounts give the per-block counts, and a pair's rank among the
+// earlier pairs of its expert is
 //     (pairs in earlier blocks) + (pairs in earlier waves of this block)
-//     + popcount(mask of its wave & lanes below it).
-// Pass 1 writes per-block count rows to the workspace; pass 2 lets every
-// block sum the rows before it (and all rows, for the totals and the
-// exclusive scan over experts) and then writes pos / recv_src.  When a single
-// block covers all tokens both passes run in one launch with no workspace.
+//     + popcount(its wave's mask & lanes below it).
+// Pass 1 writes per-block count rows to the workspace.  Pass 2 pulls the
+// whole count table into LDS in one cooperative sweep, so every block gets
+// its prefix, the totals and the exclusive scan over experts without another
+// launch, then writes pos / recv_src.  When one block covers all tokens both
+// passes run in a single launch with no workspace.
 #include "moe_device.hpp"
 #include "moe_internal.hpp"
 
@@ -27,6 +28,7 @@ namespace {
 constexpr int kLayoutThreads = 256;
 constexpr int kLayoutWaves = kLayoutThreads / kWave;
 constexpr int kTokensPerLayoutBlock = kLayoutThreads;  // one token per thread
+constexpr int kTableCacheInts = 8192;                  // count rows kept in LDS (32 KiB)
 
 struct LayoutArgs {
     const int32_t* idx;
@@ -35,30 +37,52 @@ struct LayoutArgs {
     int32_t* ws_rcnt;   // [NB, R] per-block distinct-token rank counts
     int32_t* ws_bad;    // [NB]    per-block bad-index flag
     int T, E, k, R, C, NB;
+    int tab_ints;       // LDS ints reserved for the cached count table (0: none)
 };
 
-// LDS: emask[kLayoutWaves][E], rmask[kLayoutWaves][R] (u64), then int32
-// scratch of 3*E + 1 words (block prefix, totals, exclusive offsets).
-__host__ __device__ inline size_t layout_lds_bytes(int E, int R) {
-    return sizeof(uint64_t) * (size_t)kLayoutWaves * (E + R) + sizeof(int32_t) * (3 * (size_t)E + 1);
-}
+// A token's k expert indices, loaded with 16/8-byte vector loads when k is a
+// compile-time 8, 4 or 2 (KT); KT = 0 handles any k up to 64 in a loop.
+template <int KT>
+struct TokenRow {
+    static constexpr int N = KT > 0 ? KT : 1;
+    int e[N];
+    __device__ __forceinline__ void load(const int32_t* row) {
+        if constexpr (KT % 4 == 0) {
+#pragma unroll
+            for (int q = 0; q < KT; q += 4) {
+                const int4 v = *(const int4*)(row + q);
+                e[q] = v.x; e[q + 1] = v.y; e[q + 2] = v.z; e[q + 3] = v.w;
+            }
+        } else if constexpr (KT == 2) {
+            const int2 v = *(const int2*)row;
+            e[0] = v.x; e[1] = v.y;
+        } else if constexpr (KT > 0) {
+#pragma unroll
+            for (int q = 0; q < KT; ++q) e[q] = row[q];
+        }
+    }
+};
 
-// Builds the masks of this block's tokens; returns 1 in any thread that saw a
-// bad index.
-__device__ int build_masks(const LayoutArgs& a, uint64_t* emask, uint64_t* rmask) {
+// Builds the lane masks of this block's tokens.  Returns 1 in any thread that
+// saw an index outside [0, E) or an index repeated inside its token.
+template <int KT>
+__device__ int build_masks(const LayoutArgs& a, uint64_t* emask, uint64_t* rmask, const TokenRow<KT>& tr,
+                           bool have) {
     const int tid = threadIdx.x;
     for (int i = tid; i < kLayoutWaves * a.E; i += kLayoutThreads) emask[i] = 0;
     for (int i = tid; i < kLayoutWaves * a.R; i += kLayoutThreads) rmask[i] = 0;
     __syncthreads();
     const int w = tid >> 6, lane = tid & 63;
-    const int t = blockIdx.x * kTokensPerLayoutBlock + tid;
     const int Er = a.E / a.R;
     const uint64_t bit = 1ull << lane;
     int bad = 0;
-    if (t < a.T) {
-        const int32_t* row = a.idx + (size_t)t * a.k;
-        for (int j = 0; j < a.k; ++j) {
-            const int e = row[j];
+    if (have) {
+        const int t = blockIdx.x * kTokensPerLayoutBlock + tid;
+        const int kk = KT > 0 ? KT : a.k;
+#pragma unroll
+        for (int j = 0; j < (KT > 0 ? KT : 64); ++j) {
+            if (KT == 0 && j >= kk) break;
+            const int e = KT > 0 ? tr.e[j] : a.idx[(size_t)t * a.k + j];
             if (e < 0 || e >= a.E) {
                 bad = 1;
                 continue;
@@ -80,71 +104,124 @@ __device__ __forceinline__ int block_count(const uint64_t* mask, int stride, int
 }
 
 // Pass 1: per-block count rows.
+template <int KT>
 __global__ __launch_bounds__(kLayoutThreads) void layout_count_kernel(LayoutArgs a) {
     extern __shared__ uint64_t lds[];
     uint64_t* emask = lds;
     uint64_t* rmask = lds + kLayoutWaves * a.E;
-    const int bad = build_masks(a, emask, rmask);
+    const int t = blockIdx.x * kTokensPerLayoutBlock + threadIdx.x;
+    const bool have = t < a.T;
+    TokenRow<KT> tr;
+    if (have) tr.load(a.idx + (size_t)t * a.k);
+    const int bad = build_masks<KT>(a, emask, rmask, tr, have);
     const int b = blockIdx.x;
-    for (int e = threadIdx.x; e < a.E; e += kLayoutThreads)
-        a.ws_cnt[(size_t)b * a.E + e] = block_count(emask, a.E, e);
+    for (int e = threadIdx.x; e < a.E; e += kLayoutThreads) a.ws_cnt[(size_t)b * a.E + e] = block_count(emask, a.E, e);
     for (int r = threadIdx.x; r < a.R; r += kLayoutThreads)
         a.ws_rcnt[(size_t)b * a.R + r] = block_count(rmask, a.R, r);
     const int any_bad = __syncthreads_or(bad);
     if (threadIdx.x == 0) a.ws_bad[b] = any_bad;
 }
 
-// Exclusive scan of tot[0..E) into off[0..E] (off[E] = total), block-wide.
+// Inclusive scan of one value per lane across a wave.
+__device__ __forceinline__ int wave_inclusive_scan(int v) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int o = __shfl_up(v, d, 64);
+        if (lane >= d) v += o;
+    }
+    return v;
+}
+
+// Exclusive scan of tot[0..E) into off[0..E] (off[E] = total), block-wide:
+// each thread owns a run of ceil(E/256) experts.
 __device__ void block_exclusive_scan(const int32_t* tot, int32_t* off, int E) {
-    // each thread scans a contiguous run of experts; then a scan of the run sums
-    __shared__ int32_t part[kLayoutThreads];
-    const int tid = threadIdx.x;
+    __shared__ int32_t wave_tot[kLayoutWaves];
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
     const int per = (E + kLayoutThreads - 1) / kLayoutThreads;
     const int lo = min(tid * per, E), hi = min(lo + per, E);
     int s = 0;
     for (int e = lo; e < hi; ++e) s += tot[e];
-    part[tid] = s;
+    const int inc = wave_inclusive_scan(s);
+    if (lane == 63) wave_tot[w] = inc;
     __syncthreads();
-    // Hillis-Steele over 256 partial sums
-    for (int d = 1; d < kLayoutThreads; d <<= 1) {
-        const int v = (tid >= d) ? part[tid - d] : 0;
-        __syncthreads();
-        part[tid] += v;
-        __syncthreads();
-    }
-    int run = (tid == 0) ? 0 : part[tid - 1];
+    int base = 0;
+#pragma unroll
+    for (int q = 0; q < kLayoutWaves; ++q)
+        if (q < w) base += wave_tot[q];
+    int run = base + inc - s;
     for (int e = lo; e < hi; ++e) {
         off[e] = run;
         run += tot[e];
     }
-    if (tid == kLayoutThreads - 1) off[E] = part[kLayoutThreads - 1];
+    if (tid == kLayoutThreads - 1) off[E] = run;
     __syncthreads();
 }
 
 // Pass 2 (FUSED: the only block, counts taken from its own masks).
-template <bool FUSED>
+template <int KT, bool FUSED>
 __global__ __launch_bounds__(kLayoutThreads) void layout_position_kernel(LayoutArgs a) {
     extern __shared__ uint64_t lds[];
     uint64_t* emask = lds;
     uint64_t* rmask = lds + kLayoutWaves * a.E;
-    int32_t* pre = (int32_t*)(rmask + kLayoutWaves * a.R);  // [E] pairs in earlier blocks
+    int32_t* tab = (int32_t*)(rmask + kLayoutWaves * a.R);  // cached count rows (16-byte aligned)
+    int32_t* pre = tab + a.tab_ints;                         // [E] pairs in earlier blocks
     int32_t* tot = pre + a.E;                                // [E] totals
     int32_t* off = tot + a.E;                                // [E+1] exclusive scan
 
     const int b = blockIdx.x, tid = threadIdx.x;
-    const int bad_here = build_masks(a, emask, rmask);
+    const int t = b * kTokensPerLayoutBlock + tid;
+    const bool have = t < a.T;
+    TokenRow<KT> tr;
+    if (have) tr.load(a.idx + (size_t)t * a.k);
 
-    // ---- block prefix and totals per expert ------------------------------
+    // ---- pull the count tables (all blocks' rows) into LDS -----------------
+    // [NB*E] expert counts, then [NB*R] rank counts, then [NB] bad flags: one
+    // cooperative sweep of independent loads, issued before any is used.
+    const int nE = a.NB * a.E, nR = a.NB * a.R;
+    const bool cached = !FUSED && nE + nR + a.NB <= a.tab_ints;
+    if (cached) {
+        const int n = nE + nR + a.NB;  // the three arrays are contiguous in the workspace
+        if ((n & 3) == 0) {
+            const int4* src = (const int4*)a.ws_cnt;
+            int4* dst = (int4*)tab;
+            for (int i = tid; i < n / 4; i += kLayoutThreads) dst[i] = src[i];
+        } else {
+            for (int i = tid; i < n; i += kLayoutThreads) tab[i] = a.ws_cnt[i];
+        }
+    }
+    const int bad_here = build_masks<KT>(a, emask, rmask, tr, have);  // contains __syncthreads
+
+    // ---- block prefix and totals per expert -------------------------------
     for (int e = tid; e < a.E; e += kLayoutThreads) {
         if (FUSED) {
             pre[e] = 0;
             tot[e] = block_count(emask, a.E, e);
         } else {
             int p = 0, s = 0;
-            for (int bb = 0; bb < a.NB; ++bb) {
-                const int c = a.ws_cnt[(size_t)bb * a.E + e];
-                if (bb < b) p += c;
-                s += c;
+            if (cached) {
+                for (int bb = 0; bb < a.NB; ++bb) {
+                    const int c = tab[bb * a.E + e];
+                    p += (bb < b) ? c : 0;
+                    s += c;
+                }
+            } else {
+                int bb = 0;
+                for (; bb + 8 <= a.NB; bb += 8) {
+                    int c[8];
+#pragma unroll
+                    for (int q = 0; q < 8; ++q) c[q] = a.ws_cnt[(size_t)(bb + q) * a.E + e];
+#pragma unroll
+                    for (int q = 0; q < 8; ++q) {
+                        p += (bb + q < b) ? c[q] : 0;
+                        s += c[q];
+                    }
+                }
+                for (; bb < a.NB; ++bb) {
+                    const int c = a.ws_cnt[(size_t)bb * a.E + e];
+                    p += (bb < b) ? c : 0;
+                    s += c;
+                }
             }
             pre[e] = p;
             tot[e] = s;
@@ -162,6 +239,8 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_position_kernel(LayoutA
             int c = 0;
             if (FUSED) {
                 c = block_count(rmask, a.R, r);
+            } else if (cached) {
+                for (int bb = 0; bb < a.NB; ++bb) c += tab[nE + bb * a.R + r];
             } else {
                 for (int bb = 0; bb < a.NB; ++bb) c += a.ws_rcnt[(size_t)bb * a.R + r];
             }
@@ -176,32 +255,49 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_position_kernel(LayoutA
             if (bad_here) f |= 2;
         } else {
             for (int bb = tid; bb < a.NB; bb += kLayoutThreads)
-                if (a.ws_bad[bb]) f |= 2;
+                if (cached ? tab[nE + nR + bb] : a.ws_bad[bb]) f |= 2;
         }
         const int any_over = __syncthreads_or(f & 1);
         const int any_bad = __syncthreads_or(f & 2);
         if (tid == 0) a.flags[0] = (any_over ? 1 : 0) | (any_bad ? 2 : 0);
     }
 
-    // ---- positions --------------------------------------------------------
+    // ---- positions ----------------------------------------------------------
     const int w = tid >> 6, lane = tid & 63;
-    const int t = b * kTokensPerLayoutBlock + tid;
     const uint64_t below = (1ull << lane) - 1ull;
-    if (t < a.T) {
-        const int32_t* row = a.idx + (size_t)t * a.k;
-        for (int j = 0; j < a.k; ++j) {
-            const int e = row[j];
+    if (have) {
+        const int kk = KT > 0 ? KT : a.k;
+        int32_t* prow = a.pos + (size_t)t * a.k;
+        int pv[KT > 0 ? KT : 1];
+#pragma unroll
+        for (int j = 0; j < (KT > 0 ? KT : 64); ++j) {
+            if (KT == 0 && j >= kk) break;
+            const int e = KT > 0 ? tr.e[j] : a.idx[(size_t)t * a.k + j];
             int32_t p = -1;
             if (e >= 0 && e < a.E) {
                 int rank = pre[e] + __popcll(emask[w * a.E + e] & below);
-                for (int ww = 0; ww < w; ++ww) rank += __popcll(emask[ww * a.E + e]);
+#pragma unroll
+                for (int ww = 0; ww < kLayoutWaves - 1; ++ww)
+                    if (ww < w) rank += __popcll(emask[ww * a.E + e]);
                 if (a.C == 0)
                     p = off[e] + rank;
                 else if (rank < a.C)
                     p = e * a.C + rank;
             }
-            a.pos[(size_t)t * a.k + j] = p;
             if (p >= 0) a.recv_src[p] = t * a.k + j;
+            if constexpr (KT > 0)
+                pv[j] = p;
+            else
+                prow[j] = p;
+        }
+        if constexpr (KT % 4 == 0 && KT > 0) {
+#pragma unroll
+            for (int q = 0; q < KT; q += 4) *(int4*)(prow + q) = make_int4(pv[q], pv[q + 1], pv[q + 2], pv[q + 3]);
+        } else if constexpr (KT == 2) {
+            *(int2*)prow = make_int2(pv[0], pv[1]);
+        } else if constexpr (KT > 0) {
+#pragma unroll
+            for (int q = 0; q < KT; ++q) prow[q] = pv[q];
         }
     }
 
@@ -214,6 +310,30 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_position_kernel(LayoutA
     }
 }
 
+size_t lds_bytes(int E, int R, bool with_table) {
+    return sizeof(uint64_t) * (size_t)kLayoutWaves * (E + R) + (with_table ? sizeof(int32_t) * kTableCacheInts : 0) +
+           sizeof(int32_t) * (3 * (size_t)E + 1);
+}
+
+template <int KT>
+hipError_t launch_kt(LayoutArgs a, hipStream_t stream) {
+    if (a.NB <= 1) {
+        a.tab_ints = 0;
+        hipLaunchKernelGGL((layout_position_kernel<KT, true>), dim3(1), dim3(kLayoutThreads),
+                           lds_bytes(a.E, a.R, false), stream, a);
+        return hipGetLastError();
+    }
+    hipLaunchKernelGGL((layout_count_kernel<KT>), dim3(a.NB), dim3(kLayoutThreads),
+                       sizeof(uint64_t) * (size_t)kLayoutWaves * (a.E + a.R), stream, a);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    const bool table = a.NB * (a.E + a.R + 1) <= kTableCacheInts;
+    a.tab_ints = table ? kTableCacheInts : 0;
+    hipLaunchKernelGGL((layout_position_kernel<KT, false>), dim3(a.NB), dim3(kLayoutThreads),
+                       lds_bytes(a.E, a.R, table), stream, a);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 size_t layout_workspace_bytes(int T, int E, int R) {
@@ -222,8 +342,8 @@ size_t layout_workspace_bytes(int T, int E, int R) {
 }
 
 hipError_t launch_layout(const int32_t* idx, int32_t* cnt_e, int32_t* cnt_r, int32_t* off_e, int32_t* off_r,
-                         int32_t* pos, int32_t* recv_src, int32_t* flags, void* workspace, int T, int E,
-                         int k, int R, int C, hipStream_t stream) {
+                         int32_t* pos, int32_t* recv_src, int32_t* flags, void* workspace, int T, int E, int k,
+                         int R, int C, hipStream_t stream) {
     const int NB = (T + kTokensPerLayoutBlock - 1) / kTokensPerLayoutBlock;
     LayoutArgs a{};
     a.idx = idx;
@@ -240,23 +360,19 @@ hipError_t launch_layout(const int32_t* idx, int32_t* cnt_e, int32_t* cnt_r, int
     a.R = R;
     a.C = C;
     a.NB = NB > 0 ? NB : 1;
-    const size_t lds = layout_lds_bytes(E, R);
-    if (NB <= 1) {
-        hipLaunchKernelGGL((layout_position_kernel<true>), dim3(1), dim3(kLayoutThreads), lds, stream, a);
-        return hipGetLastError();
-    }
     int32_t* ws = (int32_t*)workspace;
     a.ws_cnt = ws;
-    a.ws_rcnt = ws + (size_t)NB * E;
-    a.ws_bad = ws + (size_t)NB * (E + R);
-    hipLaunchKernelGGL(layout_count_kernel, dim3(NB), dim3(kLayoutThreads),
-                       sizeof(uint64_t) * (size_t)kLayoutWaves * (E + R), stream, a);
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
-    hipLaunchKernelGGL((layout_position_kernel<false>), dim3(NB), dim3(kLayoutThreads), lds, stream, a);
-    return hipGetLastError();
+    a.ws_rcnt = ws + (size_t)a.NB * E;
+    a.ws_bad = ws + (size_t)a.NB * (E + R);
+    // vector paths need 16-byte aligned rows (k = 8, 4) or 8-byte (k = 2)
+    const bool al16 = ((uintptr_t)idx % 16 == 0) && ((uintptr_t)pos % 16 == 0);
+    const bool al8 = ((uintptr_t)idx % 8 == 0) && ((uintptr_t)pos % 8 == 0);
+    if (k == 8 && al16) return launch_kt<8>(a, stream);
+    if (k == 4 && al16) return launch_kt<4>(a, stream);
+    if (k == 2 && al8) return launch_kt<2>(a, stream);
+    return launch_kt<0>(a, stream);
 }
 
-size_t layout_lds_bytes_host(int E, int R) { return layout_lds_bytes(E, R); }
+size_t layout_lds_bytes_host(int E, int R) { return lds_bytes(E, R, true); }
 
 }  // namespace cgl

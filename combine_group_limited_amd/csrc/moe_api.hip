@@ -147,7 +147,7 @@ moe_status moe_get_layout(const moe_layout_cfg* c, const int32_t* topk_idx, int3
     if (!workspace || workspace_bytes < need)
         return fail(MOE_ERR_WORKSPACE, "layout: workspace needs %zu bytes, got %zu", need,
                     workspace ? workspace_bytes : (size_t)0);
-    if (!aligned(workspace, 4)) return fail(MOE_ERR_INVALID, "layout: workspace must be 4-byte aligned");
+    if (!aligned(workspace, 16)) return fail(MOE_ERR_INVALID, "layout: workspace must be 16-byte aligned");
     return hip_status(launch_layout(topk_idx, cnt_e, cnt_r, off_e, off_r, pos, recv_src, flags, workspace, T,
                                     c->num_experts, c->topk, c->num_ranks, c->capacity, (hipStream_t)stream),
                       "layout launch");

@@ -11,9 +11,30 @@ namespace cgl {
 
 constexpr int kWave = 64;
 
+// Index of the calling wave within its block, as a wave-uniform (scalar)
+// value: lets the compiler keep per-wave addresses in SGPRs and use scalar
+// loads for per-wave data.
+__device__ __forceinline__ int wave_in_block() {
+    return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+}
+
 // Native vector types (usable with the nontemporal load/store builtins).
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Global loads/stores of streams that are touched once: NT = 1 marks them
+// non-temporal (streaming) so they do not displace reusable lines.
+template <int NT, typename V>
+__device__ __forceinline__ V load_stream(const V* p) {
+    if constexpr (NT) return __builtin_nontemporal_load(p);
+    else return *p;
+}
+
+template <int NT, typename V>
+__device__ __forceinline__ void store_stream(V v, V* p) {
+    if constexpr (NT) __builtin_nontemporal_store(v, p);
+    else *p = v;
+}
 
 // ---------------------------------------------------------------------------
 // fp32 exponential used for router scores.  Router selection must agree bit
@@ -25,10 +46,11 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 //   result = p * 2^n (exact, v_ldexp_f32)
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float exp_fixed(float z) {
-    if (z >= 80.0f) return __builtin_inff();
-    if (z <= -80.0f) return 0.0f;
-    const float n = __builtin_rintf(z * 1.44269504f);
-    float r = __builtin_fmaf(-n, 0x1.62e4p-1f, z);
+    // branch-free: evaluate on the clamped argument, then select the clamp
+    // results (identical to returning early for |z| >= 80)
+    const float zc = __builtin_fminf(__builtin_fmaxf(z, -80.0f), 80.0f);
+    const float n = __builtin_rintf(zc * 1.44269504f);
+    float r = __builtin_fmaf(-n, 0x1.62e4p-1f, zc);
     r = __builtin_fmaf(-n, 1.4286068e-6f, r);
     float p = 0x1.a01a02p-13f;                 // 1/5040
     p = __builtin_fmaf(p, r, 0x1.6c16c2p-10f); // 1/720
@@ -38,7 +60,8 @@ __device__ __forceinline__ float exp_fixed(float z) {
     p = __builtin_fmaf(p, r, 0.5f);
     p = __builtin_fmaf(p, r, 1.0f);
     p = __builtin_fmaf(p, r, 1.0f);
-    return __builtin_ldexpf(p, (int)n);
+    const float e = __builtin_ldexpf(p, (int)n);
+    return (z >= 80.0f) ? __builtin_inff() : ((z <= -80.0f) ? 0.0f : e);
 }
 
 __device__ __forceinline__ float sigmoid_fixed(float x) {
@@ -134,6 +157,49 @@ __device__ __forceinline__ uint32_t row16_max_u32(uint32_t v) {
     v = max(v, dpp32<0x141>(v));
     v = max(v, dpp32<0x140>(v));
     return v;
+}
+
+// DPP exchange of a float within rows of 16 lanes (same controls as dpp32).
+template <int CTRL>
+__device__ __forceinline__ float dppf(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// Max of floats over aligned segments of W lanes (W a power of two <= 64);
+// every lane of a segment receives it.  Inputs are finite or -inf.
+template <int W>
+__device__ __forceinline__ float seg_maxf(float v) {
+    if constexpr (W >= 2) v = __builtin_fmaxf(v, dppf<0xB1>(v));
+    if constexpr (W >= 4) v = __builtin_fmaxf(v, dppf<0x4E>(v));
+    if constexpr (W >= 8) v = __builtin_fmaxf(v, dppf<0x141>(v));
+    if constexpr (W >= 16) v = __builtin_fmaxf(v, dppf<0x140>(v));
+    const int lane = (int)__lane_id();
+    if constexpr (W >= 32) v = __builtin_fmaxf(v, __int_as_float(__builtin_amdgcn_ds_bpermute((lane ^ 16) << 2, __float_as_int(v))));
+    if constexpr (W >= 64) v = __builtin_fmaxf(v, __int_as_float(__builtin_amdgcn_ds_bpermute((lane ^ 32) << 2, __float_as_int(v))));
+    return v;
+}
+
+// Min of unsigned values over aligned segments of W lanes.
+template <int W>
+__device__ __forceinline__ uint32_t seg_minu(uint32_t v) {
+    if constexpr (W >= 2) v = min(v, dpp32<0xB1>(v));
+    if constexpr (W >= 4) v = min(v, dpp32<0x4E>(v));
+    if constexpr (W >= 8) v = min(v, dpp32<0x141>(v));
+    if constexpr (W >= 16) v = min(v, dpp32<0x140>(v));
+    const int lane = (int)__lane_id();
+    if constexpr (W >= 32) v = min(v, bperm32(v, lane ^ 16));
+    if constexpr (W >= 64) v = min(v, bperm32(v, lane ^ 32));
+    return v;
+}
+
+// Max of floats over the whole wave, as a wave-uniform value.
+__device__ __forceinline__ float wave_maxf(float v) {
+    v = seg_maxf<16>(v);
+    const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+    const float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+    const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+    const float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+    return __builtin_fmaxf(__builtin_fmaxf(a, b), __builtin_fmaxf(c, d));
 }
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }

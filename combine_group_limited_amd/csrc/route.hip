@@ -7,12 +7,16 @@
 // then top-8 experts).
 //
 // Lane l holds experts l*EPL .. l*EPL+EPL-1 (EPL = ceil(E/64), at most 8), so
-// a 256-expert row is one coalesced 1 KiB read.  Every selection is a max over
-// 64-bit keys (score order, then lower index), which makes the choice unique
-// and equal to the host's.  With contiguous groups whose size is a multiple of
-// EPL, a group occupies an aligned power-of-two run of lanes and all group
-// scores come out of one segmented DPP reduction per round; other shapes fall
-// back to one full-wave reduction per group and round.
+// a 256-expert row is one coalesced 1 KiB read.  Each selection round is a
+// wave max of fp32 scores (v_max_f32 with DPP operands inside rows of 16, then
+// four readlanes) followed by a ballot that picks, among the lanes holding
+// that maximum, the lowest expert index -- the order "higher score first,
+// equal scores by lower index" (with -0 == +0), the same order the host uses.
+// Chosen and excluded experts are set to -inf.  With contiguous groups whose
+// size is a multiple of EPL, a group occupies an aligned power-of-two run of
+// lanes and all group scores come out of segmented DPP reductions; other
+// shapes reduce once per group.  Group selection ranks each group against all
+// others in one pass.
 #include "moe_device.hpp"
 #include "moe_internal.hpp"
 
@@ -27,50 +31,74 @@ struct RouteArgs {
 };
 
 constexpr int kTokensPerBlock = 4;  // one wave per token, 256 threads
+constexpr float kNegInf = -__builtin_huge_valf();
 
-// Group scores with groups aligned to LPG-lane segments.  Returns, in lane
-// gamma (< G), the score of group gamma.
-template <int EPL, int LPG>
-__device__ __forceinline__ float group_scores_segmented(const uint64_t (&key)[EPL], int n, int lane) {
-    uint32_t taken = 0;
-    float sum = 0.0f;
-    for (int r = 0; r < n; ++r) {
-        uint64_t best = 0;
+// Index (0..EPL-1) of the first of a lane's values equal to m, or EPL.
+template <int EPL>
+__device__ __forceinline__ uint32_t first_equal(const float (&v)[EPL], float m) {
+    uint32_t c = EPL;
 #pragma unroll
-        for (int i = 0; i < EPL; ++i)
-            if (!(taken & (1u << i))) best = umax64(best, key[i]);
-        best = seg_max64<LPG>(best);
-        const float v = key_value(best);
-        sum = (r == 0) ? v : sum + v;
-        const uint32_t e = key_index(best);  // 0xFFFFFFFF when the segment is empty
-        if (e / EPL == (uint32_t)lane) taken |= 1u << (e % EPL);
-    }
-    // segment gamma starts at lane gamma*LPG; move its sum to lane gamma
-    const int src = (lane * LPG) & 63;
-    return __uint_as_float(bperm32(__float_as_uint(sum), src));
+    for (int i = EPL - 1; i >= 0; --i)
+        if (v[i] == m) c = (uint32_t)i;
+    return c;
 }
 
-// General group scores: G * n full-wave reductions.
+// Removes (sets to -inf) element i of a lane's values.
 template <int EPL>
-__device__ __forceinline__ float group_scores_general(const uint64_t (&key)[EPL], int E, int G, int n,
-                                                      int lane) {
+__device__ __forceinline__ void drop(float (&v)[EPL], uint32_t i) {
+#pragma unroll
+    for (int q = 0; q < EPL; ++q)
+        if ((uint32_t)q == i) v[q] = kNegInf;
+}
+
+// Group score (sum of the n largest) of every group, groups aligned to
+// LPG-lane segments: every lane of segment gamma receives the score of group
+// gamma.
+template <int EPL, int LPG>
+__device__ __forceinline__ float group_scores_segmented(const float (&s)[EPL], int n, int lane) {
+    float v[EPL];
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) v[i] = s[i];
+    float sum = 0.0f;
+    for (int r = 0; r < n; ++r) {
+        float m = v[0];
+#pragma unroll
+        for (int i = 1; i < EPL; ++i) m = __builtin_fmaxf(m, v[i]);
+        m = seg_maxf<LPG>(m);
+        sum = (r == 0) ? m : sum + m;
+        // lowest expert of the segment holding the maximum
+        const uint32_t c = first_equal<EPL>(v, m);
+        const uint32_t e = (c < EPL) ? (uint32_t)lane * EPL + c : 0xFFFFFFFFu;
+        const uint32_t emin = seg_minu<LPG>(e);
+        if (emin / EPL == (uint32_t)lane) drop<EPL>(v, emin % EPL);
+    }
+    return sum;
+}
+
+// Group scores for any contiguous grouping: G * n full-wave rounds.  Returns
+// in lane gamma (< G) the score of group gamma.
+template <int EPL>
+__device__ __forceinline__ float group_scores_general(const float (&s)[EPL], int E, int G, int n, int lane) {
     const int Eg = E / G;
     float mine = 0.0f;
     for (int gr = 0; gr < G; ++gr) {
-        uint32_t taken = 0;
+        float v[EPL];
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) {
+            const int e = lane * EPL + i;
+            v[i] = (e < E && e / Eg == gr) ? s[i] : kNegInf;
+        }
         float sum = 0.0f;
         for (int r = 0; r < n; ++r) {
-            uint64_t best = 0;
+            float m = v[0];
 #pragma unroll
-            for (int i = 0; i < EPL; ++i) {
-                const int e = lane * EPL + i;
-                if (e < E && e / Eg == gr && !(taken & (1u << i))) best = umax64(best, key[i]);
-            }
-            best = wave_max64(best);
-            const float v = key_value(best);
-            sum = (r == 0) ? v : sum + v;
-            const uint32_t e = key_index(best);
-            if (e / EPL == (uint32_t)lane) taken |= 1u << (e % EPL);
+            for (int i = 1; i < EPL; ++i) m = __builtin_fmaxf(m, v[i]);
+            m = wave_maxf(m);
+            sum = (r == 0) ? m : sum + m;
+            const uint32_t c = first_equal<EPL>(v, m);
+            const uint64_t bal = __ballot(c < EPL);
+            const int src = __builtin_ctzll(bal);
+            if (lane == src) drop<EPL>(v, c);
         }
         if (lane == gr) mine = sum;
     }
@@ -80,73 +108,75 @@ __device__ __forceinline__ float group_scores_general(const uint64_t (&key)[EPL]
 template <int EPL, int LPG>
 __global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
     const int lane = threadIdx.x & 63;
-    const int t = blockIdx.x * kTokensPerBlock + (threadIdx.x >> 6);
+    const int t = blockIdx.x * kTokensPerBlock + wave_in_block();
     if (t >= a.T) return;  // wave-uniform
     const int E = a.E;
     const float* row = a.logits + (size_t)t * E;
 
-    float l[EPL];
-    uint64_t key[EPL];
+    // all EPL loads are issued before any is used (clamped index, no branch)
+    float l[EPL], s[EPL];
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) l[i] = row[min(lane * EPL + i, E - 1)];
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
         const int e = lane * EPL + i;
-        l[i] = (e < E) ? row[e] : 0.0f;
-        const float s = (a.score_fn == 0) ? sigmoid_fixed(l[i]) : l[i];
-        key[i] = (e < E) ? make_key(s, (uint32_t)e) : 0ull;
+        if (e >= E) l[i] = 0.0f;
+        s[i] = (e < E) ? ((a.score_fn == 0) ? sigmoid_fixed(l[i]) : l[i]) : kNegInf;
     }
 
-    // ---- group limit: keep the a.g best groups --------------------------
+    // ---- group limit: keep the a.g best groups ----------------------------
     if (a.G > 1) {
-        float gs;
-        if constexpr (LPG > 0)
-            gs = group_scores_segmented<EPL, LPG>(key, a.n, lane);
-        else
-            gs = group_scores_general<EPL>(key, E, a.G, a.n, lane);
-        uint64_t gkey = (lane < a.G) ? make_key(gs, (uint32_t)lane) : 0ull;
-        uint64_t kept = 0;  // bit gamma set: group gamma kept
-        for (int r = 0; r < a.g; ++r) {
-            const uint64_t best = wave_max64(gkey);
-            const int gr = (int)key_index(best);
-            kept |= 1ull << gr;
-            if (lane == gr) gkey = 0;
-        }
         const int Eg = E / a.G;
+        float gs;      // in lane gamma (< G): score of group gamma
+        if constexpr (LPG > 0) {
+            const float seg = group_scores_segmented<EPL, LPG>(s, a.n, lane);
+            gs = __int_as_float(__builtin_amdgcn_ds_bpermute(((lane * LPG) & 63) << 2, __float_as_int(seg)));
+        } else {
+            gs = group_scores_general<EPL>(s, E, a.G, a.n, lane);
+        }
+        // rank of each group among all groups (higher score first, then lower
+        // index); a group is kept when its rank is below topk_group
+        int rank = 0;
+        for (int q = 0; q < a.G; ++q) {
+            const float o = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gs), q));
+            rank += (o > gs || (o == gs && q < lane)) ? 1 : 0;
+        }
+        const uint64_t kept = __ballot(lane < a.G && rank < a.g);
 #pragma unroll
         for (int i = 0; i < EPL; ++i) {
             const int e = lane * EPL + i;
-            if (e < E && !((kept >> (e / Eg)) & 1ull)) key[i] = 0;
+            if (e < E && !((kept >> (e / Eg)) & 1ull)) s[i] = kNegInf;
         }
     }
 
-    // ---- top-k experts; lane j keeps slot j -------------------------------
+    // ---- top-k experts; lane j keeps slot j --------------------------------
     int my_e = 0;
     float my_v = 0.0f;   // score (sigmoid) or logit (softmax) of slot j
     float my_u = 0.0f;   // softmax numerator exp(l_j - l_0)
     float den = 0.0f;
     float l0 = 0.0f;
     for (int j = 0; j < a.k; ++j) {
-        uint64_t best = 0;
+        float m = s[0];
 #pragma unroll
-        for (int i = 0; i < EPL; ++i) best = umax64(best, key[i]);
-        best = wave_max64(best);
-        const uint32_t e = key_index(best);
-        const float v = key_value(best);
-        if (e / EPL == (uint32_t)lane) {
-#pragma unroll
-            for (int i = 0; i < EPL; ++i)
-                if ((uint32_t)i == e % EPL) key[i] = 0;
-        }
+        for (int i = 1; i < EPL; ++i) m = __builtin_fmaxf(m, s[i]);
+        m = wave_maxf(m);
+        const uint32_t c = first_equal<EPL>(s, m);
+        const uint64_t bal = __ballot(c < EPL);
+        const int src = __builtin_ctzll(bal);
+        const int ci = __builtin_amdgcn_readlane((int)c, src);
+        const int e = src * EPL + ci;
+        if (lane == src) drop<EPL>(s, (uint32_t)ci);
         if (a.score_fn == 0) {
-            den = (j == 0) ? v : den + v;
+            den = (j == 0) ? m : den + m;
         } else {
-            if (j == 0) l0 = v;
-            const float u = exp_fixed(v - l0);
+            if (j == 0) l0 = m;
+            const float u = exp_fixed(m - l0);
             den = (j == 0) ? u : den + u;
             if (lane == j) my_u = u;
         }
         if (lane == j) {
-            my_e = (int)e;
-            my_v = v;
+            my_e = e;
+            my_v = m;
         }
     }
 
@@ -161,20 +191,18 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
     } else {
         // full softmax probability: max and sum over all E logits, the sum
         // taken in expert order (a sequential chain, as the host does)
-        uint32_t mo = 0;
+        float mx = kNegInf;
 #pragma unroll
         for (int i = 0; i < EPL; ++i)
-            if (lane * EPL + i < E) mo = max(mo, float_order(l[i]));
-        uint64_t mk = wave_max64((uint64_t)mo << 32);
-        const float lmax = order_float((uint32_t)(mk >> 32));
+            if (lane * EPL + i < E) mx = __builtin_fmaxf(mx, l[i]);
+        const float lmax = wave_maxf(mx);
         float sum = 0.0f;
         for (int src = 0; src < 64; ++src) {
 #pragma unroll
             for (int i = 0; i < EPL; ++i) {
                 const int e = src * EPL + i;
                 if (e < E) {
-                    const float le = __uint_as_float(
-                        (uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(l[i]), src));
+                    const float le = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(l[i]), src));
                     const float u = exp_fixed(le - lmax);
                     sum = (e == 0) ? u : sum + u;
                 }
@@ -199,7 +227,7 @@ template <int EPL>
 hipError_t pick_lpg(const RouteArgs& a, hipStream_t s) {
     const int Eg = a.E / a.G;
     int lpg = 0;  // 0: general path
-    if (a.G > 1 && Eg % EPL == 0 && a.G <= 64) {
+    if (a.G > 1 && Eg % EPL == 0) {
         const int l = Eg / EPL;
         if ((l & (l - 1)) == 0 && l <= 64) lpg = l;
     }
@@ -217,8 +245,8 @@ hipError_t pick_lpg(const RouteArgs& a, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_route(const float* logits, int32_t* idx, float* w, int T, int E, int G, int g,
-                        int k, int n, int score_fn, int renorm, hipStream_t stream) {
+hipError_t launch_route(const float* logits, int32_t* idx, float* w, int T, int E, int G, int g, int k, int n,
+                        int score_fn, int renorm, hipStream_t stream) {
     RouteArgs a{logits, idx, w, T, E, G, g, k, n, score_fn, renorm};
     const int epl = (E + 63) / 64;
     if (epl <= 1) return pick_lpg<1>(a, stream);

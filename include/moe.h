@@ -130,7 +130,8 @@ moe_status moe_route_topk(const moe_route_cfg* cfg, const float* logits, int32_t
 /*   flags[0]   = MOE_FLAG_* bits (0 = all good)             int32 [1]      */
 /* Counts are never clamped.  If MOE_FLAG_BAD_INDEX is set the other        */
 /* outputs are unspecified (but every write stays in bounds).               */
-/* workspace: device memory of at least moe_layout_workspace_bytes(cfg).    */
+/* workspace: device memory of at least moe_layout_workspace_bytes(cfg),    */
+/* 16-byte aligned; its contents need no initialisation.                    */
 /* Limits: 1 <= E <= 512, 1 <= k <= 64, 1 <= R <= E, E % R == 0,          */
 /*         T*k < 2^31, E*C < 2^31.                                          */
 /* ------------------------------------------------------------------------ */
