@@ -18,7 +18,15 @@ namespace cgl {
 namespace {
 
 constexpr int kUnit = 512;
-constexpr int kCombineThreads = 256;
+#ifndef CGL_COMBINE_THREADS
+#define CGL_COMBINE_THREADS 256
+#endif
+// LDS bytes requested per block only to cap how many blocks share a CU
+// (0 = no cap)
+#ifndef CGL_COMBINE_LDS_CAP
+#define CGL_COMBINE_LDS_CAP 0
+#endif
+constexpr int kCombineThreads = CGL_COMBINE_THREADS;  // waves per block = threads / 64
 
 // cache policy of the y gathers and the output writes (1 = streaming)
 #ifndef CGL_COMBINE_LOAD_NT
@@ -153,10 +161,10 @@ hipError_t launch_u(CombineArgs a, hipStream_t s) {
     const int wpb = kCombineThreads / kWave;
     const unsigned blocks = (unsigned)((waves + wpb - 1) / wpb);
     switch (a.k) {
-        case 8: hipLaunchKernelGGL((combine_kernel<U, 8>), dim3(blocks), dim3(kCombineThreads), 0, s, a); break;
-        case 4: hipLaunchKernelGGL((combine_kernel<U, 4>), dim3(blocks), dim3(kCombineThreads), 0, s, a); break;
-        case 2: hipLaunchKernelGGL((combine_kernel<U, 2>), dim3(blocks), dim3(kCombineThreads), 0, s, a); break;
-        default: hipLaunchKernelGGL((combine_kernel<U, 0>), dim3(blocks), dim3(kCombineThreads), 0, s, a); break;
+        case 8: hipLaunchKernelGGL((combine_kernel<U, 8>), dim3(blocks), dim3(kCombineThreads), CGL_COMBINE_LDS_CAP, s, a); break;
+        case 4: hipLaunchKernelGGL((combine_kernel<U, 4>), dim3(blocks), dim3(kCombineThreads), CGL_COMBINE_LDS_CAP, s, a); break;
+        case 2: hipLaunchKernelGGL((combine_kernel<U, 2>), dim3(blocks), dim3(kCombineThreads), CGL_COMBINE_LDS_CAP, s, a); break;
+        default: hipLaunchKernelGGL((combine_kernel<U, 0>), dim3(blocks), dim3(kCombineThreads), CGL_COMBINE_LDS_CAP, s, a); break;
     }
     return hipGetLastError();
 }

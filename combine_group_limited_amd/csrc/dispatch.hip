@@ -22,7 +22,15 @@ namespace cgl {
 namespace {
 
 constexpr int kUnit = 512;             // channels per wave-wide 16-byte load
-constexpr int kDispatchThreads = 256;  // four waves
+#ifndef CGL_DISPATCH_THREADS
+#define CGL_DISPATCH_THREADS 256
+#endif
+// LDS bytes requested per block only to cap how many blocks share a CU
+// (0 = no cap)
+#ifndef CGL_DISPATCH_LDS_CAP
+#define CGL_DISPATCH_LDS_CAP 0
+#endif
+constexpr int kDispatchThreads = CGL_DISPATCH_THREADS;  // waves per block = threads / 64
 
 // cache policy of the x reads and the receive-buffer writes (1 = streaming).
 // Measured on MI355X at 4096 x 7168 top-8: streaming loads with ordinary
@@ -155,9 +163,9 @@ hipError_t launch_u(DispatchArgs a, bool fp8, hipStream_t s) {
     const int wpb = kDispatchThreads / kWave;
     const unsigned blocks = (unsigned)((waves + wpb - 1) / wpb);
     if (fp8)
-        hipLaunchKernelGGL((dispatch_fp8_kernel<U>), dim3(blocks), dim3(kDispatchThreads), 0, s, a);
+        hipLaunchKernelGGL((dispatch_fp8_kernel<U>), dim3(blocks), dim3(kDispatchThreads), CGL_DISPATCH_LDS_CAP, s, a);
     else
-        hipLaunchKernelGGL((dispatch_bf16_kernel<U>), dim3(blocks), dim3(kDispatchThreads), 0, s, a);
+        hipLaunchKernelGGL((dispatch_bf16_kernel<U>), dim3(blocks), dim3(kDispatchThreads), CGL_DISPATCH_LDS_CAP, s, a);
     return hipGetLastError();
 }
 

@@ -192,6 +192,31 @@ __device__ __forceinline__ uint32_t seg_minu(uint32_t v) {
     return v;
 }
 
+// Max of unsigned values over aligned segments of W lanes (W a power of two
+// <= 16 uses only DPP; 32 and 64 add permutes).
+template <int W>
+__device__ __forceinline__ uint32_t seg_maxu(uint32_t v) {
+    if constexpr (W >= 2) v = max(v, dpp32<0xB1>(v));
+    if constexpr (W >= 4) v = max(v, dpp32<0x4E>(v));
+    if constexpr (W >= 8) v = max(v, dpp32<0x141>(v));
+    if constexpr (W >= 16) v = max(v, dpp32<0x140>(v));
+    const int lane = (int)__lane_id();
+    if constexpr (W >= 32) v = max(v, bperm32(v, lane ^ 16));
+    if constexpr (W >= 64) v = max(v, bperm32(v, lane ^ 32));
+    return v;
+}
+
+// Max of unsigned values over the whole wave, as a wave-uniform value: DPP
+// inside rows of 16, then the four row results on the scalar unit.
+__device__ __forceinline__ uint32_t wave_maxu(uint32_t v) {
+    v = seg_maxu<16>(v);
+    const uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)v, 0);
+    const uint32_t b = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
+    const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)v, 32);
+    const uint32_t d = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
+    return max(max(a, b), max(c, d));
+}
+
 // Max of floats over the whole wave, as a wave-uniform value.
 __device__ __forceinline__ float wave_maxf(float v) {
     v = seg_maxf<16>(v);

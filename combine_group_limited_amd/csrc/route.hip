@@ -7,16 +7,17 @@
 // then top-8 experts).
 //
 // Lane l holds experts l*EPL .. l*EPL+EPL-1 (EPL = ceil(E/64), at most 8), so
-// a 256-expert row is one coalesced 1 KiB read.  Each selection round is a
-// wave max of fp32 scores (v_max_f32 with DPP operands inside rows of 16, then
-// four readlanes) followed by a ballot that picks, among the lanes holding
-// that maximum, the lowest expert index -- the order "higher score first,
-// equal scores by lower index" (with -0 == +0), the same order the host uses.
-// Chosen and excluded experts are set to -inf.  With contiguous groups whose
-// size is a multiple of EPL, a group occupies an aligned power-of-two run of
-// lanes and all group scores come out of segmented DPP reductions; other
-// shapes reduce once per group.  Group selection ranks each group against all
-// others in one pass.
+// a 256-expert row is one coalesced 1 KiB read.  Scores are mapped once to
+// order-preserving 32-bit keys (-0 folded onto +0; 0 marks a removed or
+// excluded expert), so every max and min below is an integer op that fuses
+// with its DPP operand.  Each selection round is a wave max (DPP inside rows
+// of 16, the four row results on the scalar unit) followed by a ballot that
+// picks, among the lanes holding that maximum, the lowest expert index -- the
+// order "higher score first, equal scores by lower index", the same order the
+// host uses.  With contiguous groups whose size is a multiple of EPL, a group
+// occupies an aligned power-of-two run of lanes and all group scores come out
+// of segmented DPP reductions; other shapes reduce once per group.  Group
+// selection ranks each group against all others in one pass.
 #include "moe_device.hpp"
 #include "moe_internal.hpp"
 
@@ -31,46 +32,47 @@ struct RouteArgs {
 };
 
 constexpr int kTokensPerBlock = 4;  // one wave per token, 256 threads
-constexpr float kNegInf = -__builtin_huge_valf();
 
-// Index (0..EPL-1) of the first of a lane's values equal to m, or EPL.
+// Index (0..EPL-1) of the first of a lane's keys equal to m, or EPL.
 template <int EPL>
-__device__ __forceinline__ uint32_t first_equal(const float (&v)[EPL], float m) {
+__device__ __forceinline__ uint32_t first_equal(const uint32_t (&v)[EPL], uint32_t m) {
     uint32_t c = EPL;
 #pragma unroll
-    for (int i = EPL - 1; i >= 0; --i)
-        if (v[i] == m) c = (uint32_t)i;
+    for (int i = EPL - 1; i >= 0; --i) c = (v[i] == m) ? (uint32_t)i : c;
     return c;
 }
 
-// Removes (sets to -inf) element i of a lane's values.
+// Removes expert e (sets its key to 0) if this lane holds it; branch-free.
 template <int EPL>
-__device__ __forceinline__ void drop(float (&v)[EPL], uint32_t i) {
+__device__ __forceinline__ void drop(uint32_t (&v)[EPL], uint32_t e, int lane) {
 #pragma unroll
-    for (int q = 0; q < EPL; ++q)
-        if ((uint32_t)q == i) v[q] = kNegInf;
+    for (int i = 0; i < EPL; ++i) v[i] = (e == (uint32_t)(lane * EPL + i)) ? 0u : v[i];
 }
 
-// Group score (sum of the n largest) of every group, groups aligned to
-// LPG-lane segments: every lane of segment gamma receives the score of group
-// gamma.
-template <int EPL, int LPG>
-__device__ __forceinline__ float group_scores_segmented(const float (&s)[EPL], int n, int lane) {
-    float v[EPL];
+template <int EPL>
+__device__ __forceinline__ uint32_t lane_max(const uint32_t (&v)[EPL]) {
+    uint32_t m = v[0];
 #pragma unroll
-    for (int i = 0; i < EPL; ++i) v[i] = s[i];
+    for (int i = 1; i < EPL; ++i) m = max(m, v[i]);
+    return m;
+}
+
+// Group score (sum of the n largest scores) of every group, groups aligned to
+// LPG-lane segments: every lane of segment gamma receives group gamma's score.
+template <int EPL, int LPG>
+__device__ __forceinline__ float group_scores_segmented(const uint32_t (&key)[EPL], int n, int lane) {
+    uint32_t v[EPL];
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) v[i] = key[i];
     float sum = 0.0f;
     for (int r = 0; r < n; ++r) {
-        float m = v[0];
-#pragma unroll
-        for (int i = 1; i < EPL; ++i) m = __builtin_fmaxf(m, v[i]);
-        m = seg_maxf<LPG>(m);
-        sum = (r == 0) ? m : sum + m;
+        const uint32_t m = seg_maxu<LPG>(lane_max<EPL>(v));
+        const float sv = order_float(m);
+        sum = (r == 0) ? sv : sum + sv;
         // lowest expert of the segment holding the maximum
         const uint32_t c = first_equal<EPL>(v, m);
         const uint32_t e = (c < EPL) ? (uint32_t)lane * EPL + c : 0xFFFFFFFFu;
-        const uint32_t emin = seg_minu<LPG>(e);
-        if (emin / EPL == (uint32_t)lane) drop<EPL>(v, emin % EPL);
+        drop<EPL>(v, seg_minu<LPG>(e), lane);
     }
     return sum;
 }
@@ -78,27 +80,26 @@ __device__ __forceinline__ float group_scores_segmented(const float (&s)[EPL], i
 // Group scores for any contiguous grouping: G * n full-wave rounds.  Returns
 // in lane gamma (< G) the score of group gamma.
 template <int EPL>
-__device__ __forceinline__ float group_scores_general(const float (&s)[EPL], int E, int G, int n, int lane) {
+__device__ __forceinline__ float group_scores_general(const uint32_t (&key)[EPL], int E, int G, int n, int lane) {
     const int Eg = E / G;
     float mine = 0.0f;
     for (int gr = 0; gr < G; ++gr) {
-        float v[EPL];
+        uint32_t v[EPL];
 #pragma unroll
         for (int i = 0; i < EPL; ++i) {
             const int e = lane * EPL + i;
-            v[i] = (e < E && e / Eg == gr) ? s[i] : kNegInf;
+            v[i] = (e < E && e / Eg == gr) ? key[i] : 0u;
         }
         float sum = 0.0f;
         for (int r = 0; r < n; ++r) {
-            float m = v[0];
-#pragma unroll
-            for (int i = 1; i < EPL; ++i) m = __builtin_fmaxf(m, v[i]);
-            m = wave_maxf(m);
-            sum = (r == 0) ? m : sum + m;
+            const uint32_t m = wave_maxu(lane_max<EPL>(v));
+            const float sv = order_float(m);
+            sum = (r == 0) ? sv : sum + sv;
             const uint32_t c = first_equal<EPL>(v, m);
             const uint64_t bal = __ballot(c < EPL);
             const int src = __builtin_ctzll(bal);
-            if (lane == src) drop<EPL>(v, c);
+            const int ci = __builtin_amdgcn_readlane((int)c, src);
+            drop<EPL>(v, (uint32_t)(src * EPL + ci), lane);
         }
         if (lane == gr) mine = sum;
     }
@@ -114,14 +115,16 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
     const float* row = a.logits + (size_t)t * E;
 
     // all EPL loads are issued before any is used (clamped index, no branch)
-    float l[EPL], s[EPL];
+    float l[EPL];
 #pragma unroll
     for (int i = 0; i < EPL; ++i) l[i] = row[min(lane * EPL + i, E - 1)];
+    uint32_t key[EPL];
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
         const int e = lane * EPL + i;
         if (e >= E) l[i] = 0.0f;
-        s[i] = (e < E) ? ((a.score_fn == 0) ? sigmoid_fixed(l[i]) : l[i]) : kNegInf;
+        const float sc = (a.score_fn == 0) ? sigmoid_fixed(l[i]) : l[i];
+        key[i] = (e < E) ? float_order(sc) : 0u;
     }
 
     // ---- group limit: keep the a.g best groups ----------------------------
@@ -129,23 +132,24 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
         const int Eg = E / a.G;
         float gs;      // in lane gamma (< G): score of group gamma
         if constexpr (LPG > 0) {
-            const float seg = group_scores_segmented<EPL, LPG>(s, a.n, lane);
+            const float seg = group_scores_segmented<EPL, LPG>(key, a.n, lane);
             gs = __int_as_float(__builtin_amdgcn_ds_bpermute(((lane * LPG) & 63) << 2, __float_as_int(seg)));
         } else {
-            gs = group_scores_general<EPL>(s, E, a.G, a.n, lane);
+            gs = group_scores_general<EPL>(key, E, a.G, a.n, lane);
         }
         // rank of each group among all groups (higher score first, then lower
         // index); a group is kept when its rank is below topk_group
+        const uint32_t gk = float_order(gs);
         int rank = 0;
         for (int q = 0; q < a.G; ++q) {
-            const float o = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gs), q));
-            rank += (o > gs || (o == gs && q < lane)) ? 1 : 0;
+            const uint32_t o = (uint32_t)__builtin_amdgcn_readlane((int)gk, q);
+            rank += (o > gk || (o == gk && q < lane)) ? 1 : 0;
         }
         const uint64_t kept = __ballot(lane < a.G && rank < a.g);
 #pragma unroll
         for (int i = 0; i < EPL; ++i) {
             const int e = lane * EPL + i;
-            if (e < E && !((kept >> (e / Eg)) & 1ull)) s[i] = kNegInf;
+            key[i] = (e < E && ((kept >> (e / Eg)) & 1ull)) ? key[i] : 0u;
         }
     }
 
@@ -156,28 +160,23 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
     float den = 0.0f;
     float l0 = 0.0f;
     for (int j = 0; j < a.k; ++j) {
-        float m = s[0];
-#pragma unroll
-        for (int i = 1; i < EPL; ++i) m = __builtin_fmaxf(m, s[i]);
-        m = wave_maxf(m);
-        const uint32_t c = first_equal<EPL>(s, m);
+        const uint32_t m = wave_maxu(lane_max<EPL>(key));
+        const uint32_t c = first_equal<EPL>(key, m);
         const uint64_t bal = __ballot(c < EPL);
         const int src = __builtin_ctzll(bal);
-        const int ci = __builtin_amdgcn_readlane((int)c, src);
-        const int e = src * EPL + ci;
-        if (lane == src) drop<EPL>(s, (uint32_t)ci);
+        const int e = src * EPL + __builtin_amdgcn_readlane((int)c, src);
+        drop<EPL>(key, (uint32_t)e, lane);
+        const float v = order_float(m);
         if (a.score_fn == 0) {
-            den = (j == 0) ? m : den + m;
+            den = (j == 0) ? v : den + v;
         } else {
-            if (j == 0) l0 = m;
-            const float u = exp_fixed(m - l0);
+            if (j == 0) l0 = v;
+            const float u = exp_fixed(v - l0);
             den = (j == 0) ? u : den + u;
-            if (lane == j) my_u = u;
+            my_u = (lane == j) ? u : my_u;
         }
-        if (lane == j) {
-            my_e = e;
-            my_v = m;
-        }
+        my_e = (lane == j) ? e : my_e;
+        my_v = (lane == j) ? v : my_v;
     }
 
     float wgt;
@@ -191,11 +190,11 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
     } else {
         // full softmax probability: max and sum over all E logits, the sum
         // taken in expert order (a sequential chain, as the host does)
-        float mx = kNegInf;
+        uint32_t mo = 0;
 #pragma unroll
         for (int i = 0; i < EPL; ++i)
-            if (lane * EPL + i < E) mx = __builtin_fmaxf(mx, l[i]);
-        const float lmax = wave_maxf(mx);
+            if (lane * EPL + i < E) mo = max(mo, float_order(l[i]));
+        const float lmax = order_float(wave_maxu(mo));
         float sum = 0.0f;
         for (int src = 0; src < 64; ++src) {
 #pragma unroll
