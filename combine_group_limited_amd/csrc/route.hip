@@ -57,6 +57,36 @@ __device__ __forceinline__ uint32_t lane_max(const uint32_t (&v)[EPL]) {
     return m;
 }
 
+// A lane's keys as a list in descending order, ties by ascending index: an
+// adjacent-compare (insertion) network that swaps only strict inversions is
+// stable, so equal keys keep their index order.  idx holds the local index.
+template <int EPL>
+__device__ __forceinline__ void sort_lane(uint32_t (&k)[EPL], uint32_t (&idx)[EPL]) {
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) idx[i] = (uint32_t)i;
+#pragma unroll
+    for (int i = 1; i < EPL; ++i)
+#pragma unroll
+        for (int j = i; j > 0; --j) {
+            const bool sw = k[j] > k[j - 1];
+            const uint32_t a = k[j - 1], b = k[j], ia = idx[j - 1], ib = idx[j];
+            k[j - 1] = sw ? b : a;
+            k[j] = sw ? a : b;
+            idx[j - 1] = sw ? ib : ia;
+            idx[j] = sw ? ia : ib;
+        }
+}
+
+// Pops the head of a lane's sorted list when adv is set (shift left, 0 in).
+template <int EPL>
+__device__ __forceinline__ void pop_head(uint32_t (&k)[EPL], uint32_t (&idx)[EPL], bool adv) {
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+        k[i] = adv ? ((i + 1 < EPL) ? k[i + 1] : 0u) : k[i];
+        idx[i] = adv ? ((i + 1 < EPL) ? idx[i + 1] : 0u) : idx[i];
+    }
+}
+
 // Group score (sum of the n largest scores) of every group, groups aligned to
 // LPG-lane segments: every lane of segment gamma receives group gamma's score.
 template <int EPL, int LPG>
@@ -73,6 +103,28 @@ __device__ __forceinline__ float group_scores_segmented(const uint32_t (&key)[EP
         const uint32_t c = first_equal<EPL>(v, m);
         const uint32_t e = (c < EPL) ? (uint32_t)lane * EPL + c : 0xFFFFFFFFu;
         drop<EPL>(v, seg_minu<LPG>(e), lane);
+    }
+    return sum;
+}
+
+// Same, from sorted lane lists: each round compares list heads only; the
+// lowest lane holding the maximum pops its head.
+template <int EPL, int LPG>
+__device__ __forceinline__ float group_scores_sorted(const uint32_t (&sk)[EPL], const uint32_t (&si)[EPL], int n,
+                                                     int lane) {
+    uint32_t k2[EPL], i2[EPL];
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+        k2[i] = sk[i];
+        i2[i] = si[i];
+    }
+    float sum = 0.0f;
+    for (int r = 0; r < n; ++r) {
+        const uint32_t m = seg_maxu<LPG>(k2[0]);
+        const float sv = order_float(m);
+        sum = (r == 0) ? sv : sum + sv;
+        const uint32_t winner = seg_minu<LPG>((k2[0] == m) ? (uint32_t)lane : 0xFFFFFFFFu);
+        pop_head<EPL>(k2, i2, winner == (uint32_t)lane);
     }
     return sum;
 }
@@ -106,8 +158,12 @@ __device__ __forceinline__ float group_scores_general(const uint32_t (&key)[EPL]
     return mine;
 }
 
+// LPG > 0: groups aligned to LPG-lane runs; LPG == 0: any contiguous
+// grouping (general path); LPG < 0: no groups.  Sorted lane lists are used
+// whenever a lane's experts all share one group (LPG != 0).
 template <int EPL, int LPG>
 __global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
+    constexpr bool kSorted = LPG != 0;
     const int lane = threadIdx.x & 63;
     const int t = blockIdx.x * kTokensPerBlock + wave_in_block();
     if (t >= a.T) return;  // wave-uniform
@@ -118,7 +174,7 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
     float l[EPL];
 #pragma unroll
     for (int i = 0; i < EPL; ++i) l[i] = row[min(lane * EPL + i, E - 1)];
-    uint32_t key[EPL];
+    uint32_t key[EPL], kidx[EPL];
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
         const int e = lane * EPL + i;
@@ -126,13 +182,14 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
         const float sc = (a.score_fn == 0) ? sigmoid_fixed(l[i]) : l[i];
         key[i] = (e < E) ? float_order(sc) : 0u;
     }
+    if constexpr (kSorted) sort_lane<EPL>(key, kidx);
 
     // ---- group limit: keep the a.g best groups ----------------------------
-    if (a.G > 1) {
+    if (LPG >= 0 && a.G > 1) {
         const int Eg = E / a.G;
         float gs;      // in lane gamma (< G): score of group gamma
         if constexpr (LPG > 0) {
-            const float seg = group_scores_segmented<EPL, LPG>(key, a.n, lane);
+            const float seg = group_scores_sorted<EPL, (LPG > 0 ? LPG : 1)>(key, kidx, a.n, lane);
             gs = __int_as_float(__builtin_amdgcn_ds_bpermute(((lane * LPG) & 63) << 2, __float_as_int(seg)));
         } else {
             gs = group_scores_general<EPL>(key, E, a.G, a.n, lane);
@@ -146,10 +203,17 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
             rank += (o > gk || (o == gk && q < lane)) ? 1 : 0;
         }
         const uint64_t kept = __ballot(lane < a.G && rank < a.g);
+        if constexpr (kSorted) {
+            // all of a lane's experts are in one group: keep or clear the list
+            const bool keep = lane * EPL < E && ((kept >> ((lane * EPL) / Eg)) & 1ull);
 #pragma unroll
-        for (int i = 0; i < EPL; ++i) {
-            const int e = lane * EPL + i;
-            key[i] = (e < E && ((kept >> (e / Eg)) & 1ull)) ? key[i] : 0u;
+            for (int i = 0; i < EPL; ++i) key[i] = keep ? key[i] : 0u;
+        } else {
+#pragma unroll
+            for (int i = 0; i < EPL; ++i) {
+                const int e = lane * EPL + i;
+                key[i] = (e < E && ((kept >> (e / Eg)) & 1ull)) ? key[i] : 0u;
+            }
         }
     }
 
@@ -160,12 +224,22 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
     float den = 0.0f;
     float l0 = 0.0f;
     for (int j = 0; j < a.k; ++j) {
-        const uint32_t m = wave_maxu(lane_max<EPL>(key));
-        const uint32_t c = first_equal<EPL>(key, m);
-        const uint64_t bal = __ballot(c < EPL);
-        const int src = __builtin_ctzll(bal);
-        const int e = src * EPL + __builtin_amdgcn_readlane((int)c, src);
-        drop<EPL>(key, (uint32_t)e, lane);
+        int e;
+        uint32_t m;
+        if constexpr (kSorted) {
+            m = wave_maxu(key[0]);
+            const uint64_t bal = __ballot(key[0] == m);
+            const int src = __builtin_ctzll(bal);
+            e = src * EPL + __builtin_amdgcn_readlane((int)kidx[0], src);
+            pop_head<EPL>(key, kidx, lane == src);
+        } else {
+            m = wave_maxu(lane_max<EPL>(key));
+            const uint32_t c = first_equal<EPL>(key, m);
+            const uint64_t bal = __ballot(c < EPL);
+            const int src = __builtin_ctzll(bal);
+            e = src * EPL + __builtin_amdgcn_readlane((int)c, src);
+            drop<EPL>(key, (uint32_t)e, lane);
+        }
         const float v = order_float(m);
         if (a.score_fn == 0) {
             den = (j == 0) ? v : den + v;
@@ -225,8 +299,9 @@ hipError_t launch(const RouteArgs& a, hipStream_t s) {
 template <int EPL>
 hipError_t pick_lpg(const RouteArgs& a, hipStream_t s) {
     const int Eg = a.E / a.G;
+    if (a.G == 1) return launch<EPL, -1>(a, s);
     int lpg = 0;  // 0: general path
-    if (a.G > 1 && Eg % EPL == 0) {
+    if (Eg % EPL == 0) {
         const int l = Eg / EPL;
         if ((l & (l - 1)) == 0 && l <= 64) lpg = l;
     }
