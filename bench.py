@@ -45,6 +45,8 @@ def parse():
     ap.add_argument("--workload", default="dsv3_prefill", choices=sorted(W.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-reps", type=int, default=0, help="oracle repetitions (0: about 10 s)")
+    ap.add_argument("--direction", choices=["forward", "backward"], default="forward",
+                    help="backward: time combine_backward -> dispatch_backward instead")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also time a plain 1 GiB device copy (reference for counters and peak)")
     return ap.parse_args()
@@ -144,6 +146,60 @@ def cpu_baseline(wl, reps: int):
             "dispatch_plus_combine_ms": round(t_dc / n * 1e3, 3)}
 
 
+def backward_main(args, wl, moe, torch, dev, sets, hev, stream):
+    """The backward pair on the routing of the first input set: combine's
+    backward (grad_out -> grad_y, grad_w) then dispatch's backward
+    (grad_recv = grad_y, identity experts -> grad_x)."""
+    idx, w = moe.route_topk(sets[0][1], wl.G, wl.g, wl.k, wl.score)
+    lay = moe.get_layout(idx, wl.E, wl.R, wl.capacity)
+    N = lay.num_recv_rows
+    g = torch.Generator(device=dev)
+    g.manual_seed(wl.seed + 2000)
+    gouts = [torch.randn((wl.T, wl.H), generator=g, device=dev).to(torch.bfloat16) for _ in range(2)]
+    grad_y = torch.empty((N, wl.H), dtype=torch.bfloat16, device=dev)
+    grad_w = torch.empty((wl.T, wl.k), dtype=torch.float32, device=dev)
+    grad_x = torch.empty((wl.T, wl.H), dtype=torch.bfloat16, device=dev)
+
+    def step(i, ev=None):
+        y = sets[i % 2][2]
+        if ev: hev.record(ev[0], stream)
+        moe.combine_backward(gouts[i % 2], y, lay.pos, w, grad_y, grad_w)
+        if ev: hev.record(ev[1], stream)
+        moe.dispatch_backward(grad_y, lay.pos, grad_x)
+        if ev: hev.record(ev[2], stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    K = args.steps
+    evs = [hev.create(3) for _ in range(K)]
+    start, end = hev.create(2)
+    if hasattr(torch.cuda, "_sleep"):
+        torch.cuda._sleep(int(2e7))
+    hev.record(start, stream)
+    for i in range(K):
+        step(i, evs[i])
+    hev.record(end, stream)
+    torch.cuda.synchronize()
+    st = np.array([[hev.ms(e[q], e[q + 1]) for q in range(2)] for e in evs]) * 1e3
+    cb_us, db_us = (float(v) for v in st.mean(0))
+    b = W.algorithmic_bytes(wl)
+    tot = b["combine_backward"] + b["dispatch_backward"]
+    res = {
+        "metric": "combine_backward+dispatch_backward effective HBM GB/s, " + wl.name,
+        "value": round(tot / ((cb_us + db_us) * 1e-6) / 1e9, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": K, "warmup": args.warmup, "ms_per_step": round(hev.ms(start, end) / K, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp32",
+        "data": "synthetic (seeded N(0,1) bf16 gradients and expert outputs)",
+        "config": {"workload": W.describe(wl), "direction": "backward"},
+        "combine_backward_us": round(cb_us, 2), "dispatch_backward_us": round(db_us, 2),
+        "combine_backward_gbps": round(b["combine_backward"] / (cb_us * 1e-6) / 1e9, 1),
+        "dispatch_backward_gbps": round(b["dispatch_backward"] / (db_us * 1e-6) / 1e9, 1),
+        "pct_of_hbm_peak": round(100 * tot / ((cb_us + db_us) * 1e-6) / 1e9 / HBM_PEAK_GBPS, 2),
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -196,6 +252,9 @@ def main():
         if ev: hev.record(ev[3], stream)
         moe.combine(y, lay.pos, wts, out)
         if ev: hev.record(ev[4], stream)
+
+    if args.direction == "backward":
+        return backward_main(args, wl, moe, torch, dev, sets, hev, stream)
 
     for i in range(args.warmup):
         step(i)

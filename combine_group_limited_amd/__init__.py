@@ -70,7 +70,10 @@ def lib() -> ctypes.CDLL:
         L.moe_dispatch.argtypes = [ctypes.POINTER(DispatchCfg), P, P, P, P, P]
         L.moe_combine.argtypes = [ctypes.POINTER(CombineCfg), P, P, P, P, P]
         L.moe_quantize_e4m3.argtypes = [P, P, ctypes.c_int64, P]
-        for f in ("moe_route_topk", "moe_get_layout", "moe_dispatch", "moe_combine", "moe_quantize_e4m3"):
+        L.moe_dispatch_backward.argtypes = [ctypes.POINTER(CombineCfg), P, P, P, P]
+        L.moe_combine_backward.argtypes = [ctypes.POINTER(CombineCfg), P, P, P, P, P, P, P]
+        for f in ("moe_route_topk", "moe_get_layout", "moe_dispatch", "moe_combine", "moe_quantize_e4m3",
+                  "moe_dispatch_backward", "moe_combine_backward"):
             getattr(L, f).restype = ctypes.c_int
         L.moe_status_string.argtypes = [ctypes.c_int]
         L.moe_status_string.restype = ctypes.c_char_p
@@ -226,6 +229,48 @@ def combine(y, pos, topk_w, out=None, units_per_wave: int = 0):
     return out
 
 
+def dispatch_backward(grad_recv, pos, out=None, units_per_wave: int = 0):
+    """Backward of dispatch: grad_recv bf16 [N,H], pos int32 [T,k] -> grad_x bf16 [T,H]."""
+    torch = _torch()
+    _need(grad_recv, "grad_recv", torch.bfloat16)
+    _need(pos, "pos", torch.int32, device=grad_recv.device)
+    T, k = pos.shape
+    N, H = grad_recv.shape
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=grad_recv.device)
+    else:
+        _need(out, "out", torch.bfloat16, (T, H), grad_recv.device)
+    cfg = CombineCfg(T, H, k, N, units_per_wave)
+    _check(lib().moe_dispatch_backward(ctypes.byref(cfg), _ptr(grad_recv), _ptr(pos), _ptr(out),
+                                       _stream(grad_recv.device)))
+    return out
+
+
+def combine_backward(grad_out, y, pos, topk_w, grad_y=None, grad_w=None, units_per_wave: int = 0):
+    """Backward of combine -> (grad_y bf16 [N,H], grad_w fp32 [T,k])."""
+    torch = _torch()
+    _need(grad_out, "grad_out", torch.bfloat16)
+    dev = grad_out.device
+    _need(y, "y", torch.bfloat16, device=dev)
+    _need(pos, "pos", torch.int32, device=dev)
+    T, k = pos.shape
+    N, H = y.shape
+    _need(grad_out, "grad_out", torch.bfloat16, (T, H), dev)
+    _need(topk_w, "topk_w", torch.float32, (T, k), dev)
+    if grad_y is None:
+        grad_y = torch.empty((N, H), dtype=torch.bfloat16, device=dev)
+    else:
+        _need(grad_y, "grad_y", torch.bfloat16, (N, H), dev)
+    if grad_w is None:
+        grad_w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    else:
+        _need(grad_w, "grad_w", torch.float32, (T, k), dev)
+    cfg = CombineCfg(T, H, k, N, units_per_wave)
+    _check(lib().moe_combine_backward(ctypes.byref(cfg), _ptr(grad_out), _ptr(y), _ptr(pos), _ptr(topk_w),
+                                      _ptr(grad_y), _ptr(grad_w), _stream(dev)))
+    return grad_y, grad_w
+
+
 def quantize_e4m3(x, out=None):
     """fp32 tensor -> uint8 E4M3FN codes of the same shape."""
     torch = _torch()
@@ -239,4 +284,4 @@ def quantize_e4m3(x, out=None):
 
 
 __all__ = ["lib", "route_topk", "get_layout", "alloc_layout", "layout_workspace_bytes", "dispatch",
-           "combine", "quantize_e4m3", "Layout", "MoeError", "FLAG_CAPACITY_OVERFLOW", "FLAG_BAD_INDEX"]
+           "combine", "dispatch_backward", "combine_backward", "quantize_e4m3", "Layout", "MoeError", "FLAG_CAPACITY_OVERFLOW", "FLAG_BAD_INDEX"]

@@ -99,7 +99,8 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(CombineArgs a)
 
     int pv = (lane < k) ? a.pos[(size_t)t * k + lane] : -1;
     if (pv >= a.N) pv = -1;                     // out of range: contributes nothing
-    const float wv = (lane < k) ? a.w[(size_t)t * k + lane] : 0.0f;
+    // no weights (the backward of dispatch): every slot weighs 1
+    const float wv = (lane < k) ? (a.w ? a.w[(size_t)t * k + lane] : 1.0f) : 0.0f;
     const uint64_t kmask = (k >= 64) ? ~0ull : ((1ull << k) - 1ull);
     const bool all_valid = __ballot(lane < k && pv >= 0) == kmask;
 

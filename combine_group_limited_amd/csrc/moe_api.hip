@@ -194,6 +194,50 @@ moe_status moe_combine(const moe_combine_cfg* c, const uint16_t* y, const int32_
                       "combine launch");
 }
 
+static moe_status check_combine_cfg(const moe_combine_cfg* c, const char* who, bool backward) {
+    if (!c) return fail(MOE_ERR_INVALID, "%s: cfg is NULL", who);
+    const int T = c->num_tokens, H = c->hidden, k = c->topk, N = c->num_recv_rows;
+    if (T < 0 || N < 0) return fail(MOE_ERR_INVALID, "%s: negative size", who);
+    if (k < 1 || k > 64) return fail(MOE_ERR_INVALID, "%s: topk %d outside [1, 64]", who, k);
+    if (H < 1 || H % 8) return fail(MOE_ERR_INVALID, "%s: hidden %d must be a positive multiple of 8", who, H);
+    const int upw = c->units_per_wave;
+    if (!(upw == 0 || upw == 1 || upw == 2 || upw == 4 || upw == 7))
+        return fail(MOE_ERR_INVALID, "%s: units_per_wave %d not in {0,1,2,4,7}", who, upw);
+    (void)backward;
+    return MOE_OK;
+}
+
+moe_status moe_dispatch_backward(const moe_combine_cfg* c, const uint16_t* grad_recv, const int32_t* pos,
+                                 uint16_t* grad_x, void* stream) {
+    moe_status st = check_combine_cfg(c, "dispatch_backward", false);
+    if (st != MOE_OK) return st;
+    const int T = c->num_tokens, N = c->num_recv_rows;
+    if (T == 0) return ok();
+    if (!pos || !grad_x || (N > 0 && !grad_recv)) return fail(MOE_ERR_INVALID, "dispatch_backward: NULL array");
+    if (!aligned(grad_recv, 16) || !aligned(grad_x, 16) || !aligned(pos, 4))
+        return fail(MOE_ERR_INVALID, "dispatch_backward: grad_recv/grad_x must be 16-byte aligned, pos 4-byte");
+    return hip_status(launch_combine(grad_recv, pos, nullptr, grad_x, T, c->hidden, c->topk, N, c->units_per_wave,
+                                     (hipStream_t)stream),
+                      "dispatch_backward launch");
+}
+
+moe_status moe_combine_backward(const moe_combine_cfg* c, const uint16_t* grad_out, const uint16_t* y,
+                                const int32_t* pos, const float* topk_w, uint16_t* grad_y, float* grad_w,
+                                void* stream) {
+    moe_status st = check_combine_cfg(c, "combine_backward", true);
+    if (st != MOE_OK) return st;
+    const int T = c->num_tokens, N = c->num_recv_rows;
+    if (T == 0) return ok();
+    if (!grad_out || !pos || !topk_w || !grad_w || (N > 0 && (!y || !grad_y)))
+        return fail(MOE_ERR_INVALID, "combine_backward: NULL array");
+    if (!aligned(grad_out, 16) || !aligned(y, 16) || !aligned(grad_y, 16) || !aligned(pos, 4) ||
+        !aligned(topk_w, 4) || !aligned(grad_w, 4))
+        return fail(MOE_ERR_INVALID, "combine_backward: row data must be 16-byte aligned, pos/w 4-byte");
+    return hip_status(launch_combine_backward(grad_out, y, pos, topk_w, grad_y, grad_w, T, c->hidden, c->topk, N,
+                                              c->units_per_wave, (hipStream_t)stream),
+                      "combine_backward launch");
+}
+
 moe_status moe_quantize_e4m3(const float* in, uint8_t* out, int64_t n, void* stream) {
     if (n < 0) return fail(MOE_ERR_INVALID, "quantize: n < 0");
     if (n == 0) return ok();

@@ -25,6 +25,10 @@ int combine_units_per_wave(int T, int H);
 hipError_t launch_combine(const uint16_t* y, const int32_t* pos, const float* w, uint16_t* out, int T, int H,
                           int k, int N, int upw, hipStream_t stream);
 
+hipError_t launch_combine_backward(const uint16_t* grad_out, const uint16_t* y, const int32_t* pos, const float* w,
+                                   uint16_t* grad_y, float* grad_w, int T, int H, int k, int N, int upw,
+                                   hipStream_t stream);
+
 hipError_t launch_quantize_e4m3(const float* in, uint8_t* out, int64_t n, hipStream_t stream);
 
 }  // namespace cgl

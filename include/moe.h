@@ -218,6 +218,34 @@ moe_status moe_combine(const moe_combine_cfg* cfg, const uint16_t* y, const int3
                        const float* topk_w, uint16_t* out, void* stream);
 
 /* ------------------------------------------------------------------------ */
+/* Backward pair.  The DeepEP V2 digest, section "training/prefill/decoding */
+/* usage", states that dispatch's backward is carried out by a combine and  */
+/* combine's backward by a dispatch.  Gradients pass straight through the   */
+/* FP8 rounding (the quantiser is treated as identity).  Both take          */
+/* moe_combine_cfg (units_per_wave: 1, 2, 4 or 7 for combine_backward).     */
+/*                                                                          */
+/* moe_dispatch_backward:                                                   */
+/*   grad_x[t, c] = bf16_rne( fp32 sum over j of grad_recv[pos[t,j], c] )   */
+/*   grad_recv bf16 [N,H] in, pos int32 [T,k] in, grad_x bf16 [T,H] out.   */
+/*   (the combine kernel with every weight 1)                               */
+/* moe_combine_backward:                                                    */
+/*   grad_y[pos[t,j], c] = bf16_rne(w[t,j] * grad_out[t,c])  (exact product,*/
+/*                         rounded once)                                    */
+/*   grad_w[t, j]        = fp32 dot of grad_out[t, :] and y[pos[t,j], :]    */
+/*   grad_out bf16 [T,H], y bf16 [N,H], pos int32 [T,k], topk_w fp32 [T,k]  */
+/*   in; grad_y bf16 [N,H], grad_w fp32 [T,k] out.  Rows of grad_y that no  */
+/*   pair addresses are not written; a pair with pos outside [0,N) gets     */
+/*   grad_w 0.                                                              */
+/* Limits: H % 8 == 0; 1 <= k <= 64.                                        */
+/* ------------------------------------------------------------------------ */
+moe_status moe_dispatch_backward(const moe_combine_cfg* cfg, const uint16_t* grad_recv, const int32_t* pos,
+                                 uint16_t* grad_x, void* stream);
+
+moe_status moe_combine_backward(const moe_combine_cfg* cfg, const uint16_t* grad_out, const uint16_t* y,
+                                const int32_t* pos, const float* topk_w, uint16_t* grad_y, float* grad_w,
+                                void* stream);
+
+/* ------------------------------------------------------------------------ */
 /* moe_quantize_e4m3 -- the element conversion moe_dispatch uses, exposed   */
 /* on its own: out[i] = E4M3FN nearest-even of in[i], magnitudes above 448  */
 /* saturate to 448, sign kept (codes for NaN inputs are unspecified).       */

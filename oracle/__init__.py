@@ -64,6 +64,10 @@ def lib():
         L.orc_dispatch.argtypes = [i32] * 5 + [P] * 4
         L.orc_combine.restype = i32
         L.orc_combine.argtypes = [i32] * 4 + [P] * 4
+        L.orc_dispatch_backward.restype = i32
+        L.orc_dispatch_backward.argtypes = [i32] * 4 + [P] * 3
+        L.orc_combine_backward.restype = i32
+        L.orc_combine_backward.argtypes = [i32] * 4 + [P] * 6
         _lib = L
     return _lib
 
@@ -180,3 +184,33 @@ def combine(y_bits: np.ndarray, pos: np.ndarray, w: np.ndarray) -> np.ndarray:
     if rc != 0:
         raise ValueError("oracle combine: invalid arguments")
     return out
+
+
+def dispatch_backward(grad_recv_bits: np.ndarray, pos: np.ndarray) -> np.ndarray:
+    """grad_recv uint16 [N,H] bf16 patterns -> grad_x uint16 [T,H]."""
+    g = np.ascontiguousarray(grad_recv_bits, dtype=np.uint16)
+    pos = np.ascontiguousarray(pos, dtype=np.int32)
+    N, H = g.shape
+    T, k = pos.shape
+    out = np.empty((T, H), dtype=np.uint16)
+    if lib().orc_dispatch_backward(T, H, k, N, _p(g), _p(pos), _p(out)) != 0:
+        raise ValueError("oracle dispatch_backward: invalid arguments")
+    return out
+
+
+def combine_backward(grad_out_bits: np.ndarray, y_bits: np.ndarray, pos: np.ndarray, w: np.ndarray,
+                     grad_y: np.ndarray | None = None):
+    """Returns (grad_y uint16 [N,H], grad_w float32 [T,k]); unaddressed rows of
+    grad_y keep the array passed in (zeros by default)."""
+    g = np.ascontiguousarray(grad_out_bits, dtype=np.uint16)
+    y = np.ascontiguousarray(y_bits, dtype=np.uint16)
+    pos = np.ascontiguousarray(pos, dtype=np.int32)
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    N, H = y.shape
+    T, k = pos.shape
+    if grad_y is None:
+        grad_y = np.zeros((N, H), dtype=np.uint16)
+    grad_w = np.empty((T, k), dtype=np.float32)
+    if lib().orc_combine_backward(T, H, k, N, _p(g), _p(y), _p(pos), _p(w), _p(grad_y), _p(grad_w)) != 0:
+        raise ValueError("oracle combine_backward: invalid arguments")
+    return grad_y, grad_w

@@ -427,3 +427,52 @@ int orc_combine(int T, int H, int k, int N, const uint16_t* y, const int32_t* po
         }
     return 0;
 }
+
+/* ------------------------------------------------------------------------ */
+/* Backward pair.  The pages state that dispatch's backward is carried out    */
+/* by a combine and combine's backward by a dispatch (DeepEP V2 digest,      */
+/* section "training/prefill/decoding usage").  Through the FP8 rounding the  */
+/* gradient passes straight (the quantiser is treated as identity).          */
+/* ------------------------------------------------------------------------ */
+int orc_dispatch_backward(int T, int H, int k, int N, const uint16_t* grad_recv,
+                          const int32_t* pos, uint16_t* grad_x)
+{
+    if (T < 0 || H <= 0 || k < 1 || N < 0) return -1;
+    for (int t = 0; t < T; ++t)
+        for (int c = 0; c < H; ++c) {
+            double acc = 0.0;
+            for (int j = 0; j < k; ++j) {
+                const int p = pos[(size_t)t * k + j];
+                if (p < 0) continue;
+                if (p >= N) return -1;
+                acc += (double)bf16_to_f32(grad_recv[(size_t)p * H + c]);
+            }
+            grad_x[(size_t)t * H + c] = orc_bf16_from_f64(acc);
+        }
+    return 0;
+}
+
+int orc_combine_backward(int T, int H, int k, int N, const uint16_t* grad_out,
+                         const uint16_t* y, const int32_t* pos, const float* w,
+                         uint16_t* grad_y, float* grad_w)
+{
+    if (T < 0 || H <= 0 || k < 1 || N < 0) return -1;
+    for (int t = 0; t < T; ++t)
+        for (int j = 0; j < k; ++j) {
+            const int p = pos[(size_t)t * k + j];
+            if (p < 0) {
+                grad_w[(size_t)t * k + j] = 0.0f;
+                continue;
+            }
+            if (p >= N) return -1;
+            const double wj = (double)w[(size_t)t * k + j];
+            double dot = 0.0;
+            for (int c = 0; c < H; ++c) {
+                const double g = (double)bf16_to_f32(grad_out[(size_t)t * H + c]);
+                grad_y[(size_t)p * H + c] = orc_bf16_from_f64(wj * g);
+                dot += g * (double)bf16_to_f32(y[(size_t)p * H + c]);
+            }
+            grad_w[(size_t)t * k + j] = (float)dot;
+        }
+    return 0;
+}

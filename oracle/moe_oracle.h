@@ -77,6 +77,19 @@ int orc_dispatch(int T, int H, int k, int N, int dtype, const uint16_t* x,
 int orc_combine(int T, int H, int k, int N, const uint16_t* y, const int32_t* pos,
                 const float* w, uint16_t* out);
 
+/* Backward of dispatch (gradients flow straight through the FP8 rounding):
+   grad_x[t,c] = bf16( sum_j grad_recv[pos[t,j], c] ), sum in double. */
+int orc_dispatch_backward(int T, int H, int k, int N, const uint16_t* grad_recv,
+                          const int32_t* pos, uint16_t* grad_x);
+
+/* Backward of combine: grad_y[pos[t,j], c] = bf16(w[t,j] * grad_out[t,c])
+   (exact product, one rounding); grad_w[t,j] = fp32( sum_c grad_out[t,c] *
+   y[pos[t,j], c] ), sum in double.  Rows of grad_y no pair addresses are not
+   written; dropped pairs (pos -1) get grad_w 0. */
+int orc_combine_backward(int T, int H, int k, int N, const uint16_t* grad_out,
+                         const uint16_t* y, const int32_t* pos, const float* w,
+                         uint16_t* grad_y, float* grad_w);
+
 #ifdef __cplusplus
 }
 #endif

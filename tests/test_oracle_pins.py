@@ -601,3 +601,100 @@ def test_workloads_follow_pages():
             assert wl.g == it["topk_group"]
         if "dispatch" in it:
             assert wl.dtype == it["dispatch"]
+
+
+# --------------------------------------------------------------------------
+# backward pair (dispatch's backward is a combine, combine's a dispatch)
+# --------------------------------------------------------------------------
+def _int_bf16(rng, shape, lo=-8, hi=8):
+    """bf16 patterns of small integers: every product and sum below is exact."""
+    return W.f32_to_bf16_bits(rng.integers(lo, hi + 1, shape).astype(np.float32))
+
+
+def _bwd_case(seed, T=24, H=64, k=3, N=None):
+    rng = np.random.default_rng(seed)
+    N = N or T * k
+    pos = rng.permutation(N).astype(np.int32)[:T * k].reshape(T, k)
+    w = rng.choice(np.float32([0.25, 0.5, 1.0, 2.0, -0.5]), (T, k)).astype(np.float32)
+    return rng, pos, w, N
+
+
+def test_combine_backward_adjoint_identity(orc):
+    """<grad_out, combine(y)> == <grad_y, y> for every y: pins the index map and
+    the weight scaling of grad_y exactly (integer data, power-of-two weights)."""
+    rng, pos, w, N = _bwd_case(31)
+    T, k = pos.shape
+    H = 64
+    g = _int_bf16(rng, (T, H))
+    y = _int_bf16(rng, (N, H))
+    gy, gw = orc.combine_backward(g, y, pos, w)
+    gf = W.bf16_bits_to_f32(g).astype(np.float64)
+    yf = W.bf16_bits_to_f32(y).astype(np.float64)
+    out_exact = np.zeros((T, H))
+    for j in range(k):
+        out_exact += w[:, j:j + 1].astype(np.float64) * yf[pos[:, j]]
+    lhs = np.sum(gf * out_exact)
+    rhs = np.sum(W.bf16_bits_to_f32(gy).astype(np.float64) * yf)
+    assert lhs == rhs
+    # grad_w: the derivative of <g, combine(w)> w.r.t. each weight (exactly linear)
+    for t in range(T):
+        for j in range(k):
+            assert gw[t, j] == np.dot(gf[t], yf[pos[t, j]])
+    assert np.sum(w.astype(np.float64) * gw) == lhs
+
+
+# w * g whose fp32 product is a bf16 midpoint while the exact product is not:
+# found by exact rational search.  w = 0x1.419d0ap+0, g = 1.859375: the fp32
+# product 2.3359375 sits halfway between 2.328125 and 2.34375 and the exact
+# product lies just below it, so the one-rounding answer is 2.328125 (rounding
+# through fp32 first would give 2.34375).
+DOUBLE_ROUNDING_CASES = [
+    (float.fromhex("0x1.419d0ap+0"), 1.859375, 2.328125),
+    (float.fromhex("0x1.874a88p+0"), 1.234375, 1.8828125),
+    (1 + 2 ** -8, 1.0, 1.0),                 # exact midpoint: ties to even
+    (1 + 2 ** -8 + 2 ** -23, 1.0, 1.0078125),  # just above the midpoint
+    (1 + 2 ** -8, 3.0, 3.015625),
+]
+
+
+def test_combine_backward_rounds_product_once(orc):
+    for wv, gv, want in DOUBLE_ROUNDING_CASES:
+        assert np.float32(wv) == wv
+        g = W.f32_to_bf16_bits(np.float32([[gv, -gv]]))
+        y = np.zeros((1, 2), np.uint16)
+        gy, _ = orc.combine_backward(g, y, np.zeros((1, 1), np.int32), np.float32([[wv]]))
+        assert np.array_equal(W.bf16_bits_to_f32(gy)[0], np.float32([want, -want])), (wv, gv)
+
+
+def test_combine_backward_k1_unit_weight_copies(orc):
+    rng, pos, _, N = _bwd_case(32, k=1)
+    g = W.f32_to_bf16_bits(rng.standard_normal((24, 64)).astype(np.float32))
+    y = W.f32_to_bf16_bits(rng.standard_normal((N, 64)).astype(np.float32))
+    gy, _ = orc.combine_backward(g, y, pos, np.ones((24, 1), np.float32))
+    assert np.array_equal(gy[pos[:, 0]], g)
+
+
+def test_dispatch_backward_adjoint_identity(orc):
+    """<grad_recv, dispatch(x)> == <grad_x, x> (BF16 dispatch is a copy)."""
+    rng, pos, _, N = _bwd_case(33, k=4)
+    T = pos.shape[0]
+    x = _int_bf16(rng, (T, 64))
+    gr = _int_bf16(rng, (N, 64))
+    rx, _ = orc.dispatch(x, pos, N, dtype=orc.BF16)
+    gx = orc.dispatch_backward(gr, pos)
+    lhs = np.sum(W.bf16_bits_to_f32(gr).astype(np.float64) * W.bf16_bits_to_f32(rx))
+    rhs = np.sum(W.bf16_bits_to_f32(gx).astype(np.float64) * W.bf16_bits_to_f32(x))
+    assert lhs == rhs
+    # and it is the combine with unit weights
+    assert np.array_equal(gx, orc.combine(gr, pos, np.ones(pos.shape, np.float32)))
+
+
+def test_backward_dropped_pairs(orc):
+    rng, pos, w, N = _bwd_case(34, k=2)
+    pos[0, 1] = -1
+    g = _int_bf16(rng, (24, 64))
+    y = _int_bf16(rng, (N, 64))
+    gy, gw = orc.combine_backward(g, y, pos, w)
+    assert gw[0, 1] == 0.0
+    gx = orc.dispatch_backward(y, pos)
+    assert np.array_equal(gx[0], y[pos[0, 0]])

@@ -149,8 +149,13 @@ def algorithmic_bytes(wl: Workload) -> dict:
     else:
         dispatch = T * H * 2 + rows * H * 2 + pairs * 4
     combine = rows * H * 2 + T * H * 2 + pairs * 8
+    # backward: grad_out read, y rows read, grad_y rows written, pos/w read,
+    # grad_w written; dispatch's backward is a combine with unit weights
+    combine_backward = T * H * 2 + 2 * rows * H * 2 + pairs * 12
+    dispatch_backward = rows * H * 2 + T * H * 2 + pairs * 4
     return dict(route=route, layout=layout, dispatch=dispatch, combine=combine,
-                total=route + layout + dispatch + combine)
+                total=route + layout + dispatch + combine,
+                combine_backward=combine_backward, dispatch_backward=dispatch_backward)
 
 
 def describe(wl: Workload) -> str:
