@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(PKG, "libcgl_moe.so")
 
 MOE_OK, MOE_ERR_INVALID, MOE_ERR_WORKSPACE, MOE_ERR_UNSUPPORTED, MOE_ERR_HIP = 0, 1, 2, 4, 5
 SCORE_FNS = {"sigmoid": 0, "softmax": 1}
-DISPATCH_DTYPES = {"fp8": 0, "bf16": 1}
+DISPATCH_DTYPES = {"fp8": 0, "bf16": 1, "fp8_pow2": 2}
 FLAG_CAPACITY_OVERFLOW, FLAG_BAD_INDEX = 1, 2
 
 
@@ -37,7 +37,7 @@ class RouteCfg(ctypes.Structure):
 
 class LayoutCfg(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
-        "num_tokens", "num_experts", "topk", "num_ranks", "capacity")]
+        "num_tokens", "num_experts", "topk", "num_ranks", "capacity", "align_rows")]
 
 
 class DispatchCfg(ctypes.Structure):
@@ -149,36 +149,44 @@ class Layout(NamedTuple):
 
 
 def layout_workspace_bytes(num_tokens: int, num_experts: int, topk: int, num_ranks: int,
-                           capacity: int = 0) -> int:
-    cfg = LayoutCfg(num_tokens, num_experts, topk, num_ranks, capacity)
+                           capacity: int = 0, align_rows: int = 0) -> int:
+    cfg = LayoutCfg(num_tokens, num_experts, topk, num_ranks, capacity, align_rows)
     n = lib().moe_layout_workspace_bytes(ctypes.byref(cfg))
     if n == 0:
         raise MoeError(MOE_ERR_INVALID, lib().moe_last_error().decode())
     return n
 
 
-def alloc_layout(num_tokens, num_experts, topk, num_ranks, capacity=0, device="cuda"):
+def recv_rows(num_tokens, num_experts, topk, capacity=0, align_rows=0) -> int:
+    """Rows of the receive buffer: E*C padded, T*k + E*(A-1) aligned, T*k packed."""
+    if capacity > 0:
+        return num_experts * capacity
+    return num_tokens * topk + (num_experts * (align_rows - 1) if align_rows > 1 else 0)
+
+
+def alloc_layout(num_tokens, num_experts, topk, num_ranks, capacity=0, device="cuda", align_rows=0):
     """Output tensors and workspace for get_layout (reusable across calls)."""
     torch = _torch()
-    N = num_experts * capacity if capacity > 0 else num_tokens * topk
+    N = recv_rows(num_tokens, num_experts, topk, capacity, align_rows)
     i32 = dict(dtype=torch.int32, device=device)
     lay = Layout(torch.empty(num_experts, **i32), torch.empty(num_ranks, **i32),
                  torch.empty(num_experts + 1, **i32), torch.empty(num_ranks + 1, **i32),
                  torch.empty((num_tokens, topk), **i32), torch.empty(N, **i32), torch.empty(1, **i32), N)
-    ws = torch.empty(layout_workspace_bytes(num_tokens, num_experts, topk, num_ranks, capacity),
+    ws = torch.empty(layout_workspace_bytes(num_tokens, num_experts, topk, num_ranks, capacity, align_rows),
                      dtype=torch.uint8, device=device)
     return lay, ws
 
 
-def get_layout(topk_idx, num_experts: int, num_ranks: int, capacity: int = 0, out=None) -> Layout:
+def get_layout(topk_idx, num_experts: int, num_ranks: int, capacity: int = 0, out=None,
+               align_rows: int = 0) -> Layout:
     """Routing layout (counts, offsets, receive rows).  out = (Layout, workspace) to reuse buffers."""
     torch = _torch()
     _need(topk_idx, "topk_idx", torch.int32)
     T, k = topk_idx.shape
     if out is None:
-        out = alloc_layout(T, num_experts, k, num_ranks, capacity, topk_idx.device)
+        out = alloc_layout(T, num_experts, k, num_ranks, capacity, topk_idx.device, align_rows)
     lay, ws = out
-    cfg = LayoutCfg(T, num_experts, k, num_ranks, capacity)
+    cfg = LayoutCfg(T, num_experts, k, num_ranks, capacity, align_rows)
     _check(lib().moe_get_layout(ctypes.byref(cfg), _ptr(topk_idx), _ptr(lay.cnt_e), _ptr(lay.cnt_r),
                                 _ptr(lay.off_e), _ptr(lay.off_r), _ptr(lay.pos), _ptr(lay.recv_src),
                                 _ptr(lay.flags), _ptr(ws), ws.numel(), _stream(topk_idx.device)))
@@ -195,7 +203,7 @@ def dispatch(x, pos, num_recv_rows: int, dtype: str = "fp8", recv_x=None, recv_s
     k = pos.shape[1]
     if pos.shape[0] != T:
         raise ValueError("pos must be [T, k]")
-    fp8 = dtype == "fp8"
+    fp8 = dtype in ("fp8", "fp8_pow2")
     if recv_x is None:
         recv_x = torch.empty((num_recv_rows, H), dtype=torch.uint8 if fp8 else torch.bfloat16,
                              device=x.device)

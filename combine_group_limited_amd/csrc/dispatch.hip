@@ -74,7 +74,24 @@ __device__ __forceinline__ uint32_t lane_absmax_bits(const u32x4& v) {
     return max(max(m0, m1), max(m2, m3));
 }
 
-template <int U>
+// Block scale.  POW2 = false: scale = a/448, inv = 448/a (IEEE divisions).
+// POW2 = true: scale = 2^e with e the smallest integer such that a <= 448*2^e;
+// writing a = m * 2^E (m in [1,2)) and 448 = 1.75 * 2^8 gives
+// e = E - 8 + (m > 1.75), read straight off a's bits, and inv = 2^-e exactly.
+template <bool POW2>
+__device__ __forceinline__ void block_scale(float aa, float& scale, float& inv) {
+    if constexpr (POW2) {
+        const uint32_t b = __float_as_uint(aa);
+        const int e = (int)(b >> 23) - 127 - 8 + ((b & 0x7FFFFFu) > 0x600000u ? 1 : 0);
+        scale = __uint_as_float((uint32_t)(e + 127) << 23);
+        inv = __uint_as_float((uint32_t)(127 - e) << 23);
+    } else {
+        scale = aa / 448.0f;
+        inv = 448.0f / aa;
+    }
+}
+
+template <int U, bool POW2>
 __global__ __launch_bounds__(kDispatchThreads) void dispatch_fp8_kernel(DispatchArgs a) {
     const int lane = threadIdx.x & 63;
     const int wave = blockIdx.x * (kDispatchThreads / kWave) + wave_in_block();
@@ -101,8 +118,8 @@ __global__ __launch_bounds__(kDispatchThreads) void dispatch_fp8_kernel(Dispatch
         const uint32_t m = row16_max_u32(lane_absmax_bits(v[u]));
         const float amax = __uint_as_float(m << 16);
         const float aa = amax > 0x1p-100f ? amax : 0x1p-100f;
-        scale[u] = aa / 448.0f;
-        const float inv = 448.0f / aa;
+        float inv;
+        block_scale<POW2>(aa, scale[u], inv);
         code[u].x = pack_e4m3x4(bf16_lo(v[u].x) * inv, bf16_hi(v[u].x) * inv, bf16_lo(v[u].y) * inv,
                                 bf16_hi(v[u].y) * inv);
         code[u].y = pack_e4m3x4(bf16_lo(v[u].z) * inv, bf16_hi(v[u].z) * inv, bf16_lo(v[u].w) * inv,
@@ -157,13 +174,17 @@ __global__ __launch_bounds__(kDispatchThreads) void dispatch_bf16_kernel(Dispatc
 }
 
 template <int U>
-hipError_t launch_u(DispatchArgs a, bool fp8, hipStream_t s) {
+hipError_t launch_u(DispatchArgs a, int dtype, hipStream_t s) {
     a.chunks = (a.units + U - 1) / U;
     const long long waves = (long long)a.T * a.chunks;
     const int wpb = kDispatchThreads / kWave;
     const unsigned blocks = (unsigned)((waves + wpb - 1) / wpb);
-    if (fp8)
-        hipLaunchKernelGGL((dispatch_fp8_kernel<U>), dim3(blocks), dim3(kDispatchThreads), CGL_DISPATCH_LDS_CAP, s, a);
+    if (dtype == 0)
+        hipLaunchKernelGGL((dispatch_fp8_kernel<U, false>), dim3(blocks), dim3(kDispatchThreads), CGL_DISPATCH_LDS_CAP,
+                           s, a);
+    else if (dtype == 2)
+        hipLaunchKernelGGL((dispatch_fp8_kernel<U, true>), dim3(blocks), dim3(kDispatchThreads), CGL_DISPATCH_LDS_CAP,
+                           s, a);
     else
         hipLaunchKernelGGL((dispatch_bf16_kernel<U>), dim3(blocks), dim3(kDispatchThreads), CGL_DISPATCH_LDS_CAP, s, a);
     return hipGetLastError();
@@ -184,7 +205,7 @@ int dispatch_units_per_wave(int T, int H) {
 }
 
 hipError_t launch_dispatch(const uint16_t* x, const int32_t* pos, void* recv_x, float* recv_scales, int T,
-                           int H, int k, int N, bool fp8, int upw, hipStream_t stream) {
+                           int H, int k, int N, int dtype, int upw, hipStream_t stream) {
     DispatchArgs a{};
     a.x = x;
     a.pos = pos;
@@ -198,12 +219,12 @@ hipError_t launch_dispatch(const uint16_t* x, const int32_t* pos, void* recv_x, 
     a.units = (H + kUnit - 1) / kUnit;
     if (upw <= 0) upw = dispatch_units_per_wave(T, H);
     switch (upw) {
-        case 14: return launch_u<14>(a, fp8, stream);
-        case 8: return launch_u<8>(a, fp8, stream);
-        case 7: return launch_u<7>(a, fp8, stream);
-        case 4: return launch_u<4>(a, fp8, stream);
-        case 2: return launch_u<2>(a, fp8, stream);
-        default: return launch_u<1>(a, fp8, stream);
+        case 14: return launch_u<14>(a, dtype, stream);
+        case 8: return launch_u<8>(a, dtype, stream);
+        case 7: return launch_u<7>(a, dtype, stream);
+        case 4: return launch_u<4>(a, dtype, stream);
+        case 2: return launch_u<2>(a, dtype, stream);
+        default: return launch_u<1>(a, dtype, stream);
     }
 }
 

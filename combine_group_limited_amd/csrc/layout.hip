@@ -36,7 +36,7 @@ struct LayoutArgs {
     int32_t* ws_cnt;    // [NB, E] per-block expert counts
     int32_t* ws_rcnt;   // [NB, R] per-block distinct-token rank counts
     int32_t* ws_bad;    // [NB]    per-block bad-index flag
-    int T, E, k, R, C, NB;
+    int T, E, k, R, C, A, NB;  // A > 1: expert regions start on multiples of A rows
     int tab_ints;       // LDS ints reserved for the cached count table (0: none)
 };
 
@@ -96,6 +96,22 @@ __device__ int build_masks(const LayoutArgs& a, uint64_t* emask, uint64_t* rmask
     return bad;
 }
 
+// recv_src[i] = -1 for i in [0, n), cooperatively by `nthreads` threads with
+// index `tid` (16-byte stores when the array is 16-byte aligned).
+__device__ void fill_minus_one(int32_t* recv_src, size_t n, size_t tid, size_t nthreads) {
+    if (((uintptr_t)recv_src & 15) == 0) {
+        const int4 m = make_int4(-1, -1, -1, -1);
+        for (size_t i = tid; i < n / 4; i += nthreads) ((int4*)recv_src)[i] = m;
+        for (size_t i = (n / 4) * 4 + tid; i < n; i += nthreads) recv_src[i] = -1;
+    } else {
+        for (size_t i = tid; i < n; i += nthreads) recv_src[i] = -1;
+    }
+}
+
+__device__ __forceinline__ size_t recv_rows(const LayoutArgs& a) {
+    return a.C > 0 ? (size_t)a.E * a.C : (size_t)a.T * a.k + (a.A > 1 ? (size_t)a.E * (a.A - 1) : 0);
+}
+
 __device__ __forceinline__ int block_count(const uint64_t* mask, int stride, int i) {
     int c = 0;
 #pragma unroll
@@ -113,6 +129,11 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_count_kernel(LayoutArgs
     const bool have = t < a.T;
     TokenRow<KT> tr;
     if (have) tr.load(a.idx + (size_t)t * a.k);
+    // padded and aligned modes: every receive row starts empty; pass 2 (a
+    // later launch) writes the occupied ones
+    if (a.C > 0 || a.A > 1)
+        fill_minus_one(a.recv_src, recv_rows(a), (size_t)blockIdx.x * kLayoutThreads + threadIdx.x,
+                       (size_t)gridDim.x * kLayoutThreads);
     const int bad = build_masks<KT>(a, emask, rmask, tr, have);
     const int b = blockIdx.x;
     for (int e = threadIdx.x; e < a.E; e += kLayoutThreads) a.ws_cnt[(size_t)b * a.E + e] = block_count(emask, a.E, e);
@@ -133,15 +154,17 @@ __device__ __forceinline__ int wave_inclusive_scan(int v) {
     return v;
 }
 
-// Exclusive scan of tot[0..E) into off[0..E] (off[E] = total), block-wide:
-// each thread owns a run of ceil(E/256) experts.
-__device__ void block_exclusive_scan(const int32_t* tot, int32_t* off, int E) {
+// Exclusive scan of tot[0..E) (each rounded up to a multiple of A when A > 1)
+// into off[0..E] (off[E] = total), block-wide: each thread owns a run of
+// ceil(E/256) experts.
+__device__ void block_exclusive_scan(const int32_t* tot, int32_t* off, int E, int A) {
     __shared__ int32_t wave_tot[kLayoutWaves];
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
     const int per = (E + kLayoutThreads - 1) / kLayoutThreads;
     const int lo = min(tid * per, E), hi = min(lo + per, E);
+    auto span = [A](int c) { return A > 1 ? (c + A - 1) / A * A : c; };
     int s = 0;
-    for (int e = lo; e < hi; ++e) s += tot[e];
+    for (int e = lo; e < hi; ++e) s += span(tot[e]);
     const int inc = wave_inclusive_scan(s);
     if (lane == 63) wave_tot[w] = inc;
     __syncthreads();
@@ -152,7 +175,7 @@ __device__ void block_exclusive_scan(const int32_t* tot, int32_t* off, int E) {
     int run = base + inc - s;
     for (int e = lo; e < hi; ++e) {
         off[e] = run;
-        run += tot[e];
+        run += span(tot[e]);
     }
     if (tid == kLayoutThreads - 1) off[E] = run;
     __syncthreads();
@@ -190,6 +213,9 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_position_kernel(LayoutA
             for (int i = tid; i < n; i += kLayoutThreads) tab[i] = a.ws_cnt[i];
         }
     }
+    // padded and aligned modes, single block: empty every receive row before
+    // the barrier in build_masks; the positions below overwrite the occupied ones
+    if (FUSED && (a.C > 0 || a.A > 1)) fill_minus_one(a.recv_src, recv_rows(a), tid, kLayoutThreads);
     const int bad_here = build_masks<KT>(a, emask, rmask, tr, have);  // contains __syncthreads
 
     // ---- block prefix and totals per expert -------------------------------
@@ -228,7 +254,7 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_position_kernel(LayoutA
         }
     }
     __syncthreads();
-    block_exclusive_scan(tot, off, a.E);
+    block_exclusive_scan(tot, off, a.E, a.A);
 
     // ---- block 0 publishes counts, offsets and flags ----------------------
     if (b == 0) {
@@ -301,13 +327,6 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_position_kernel(LayoutA
         }
     }
 
-    // ---- padded mode: mark the empty rows of experts e = b, b+NB, ... -----
-    if (a.C > 0) {
-        for (int e = b; e < a.E; e += a.NB) {
-            const int used = min(tot[e], a.C);
-            for (int r = used + tid; r < a.C; r += kLayoutThreads) a.recv_src[(size_t)e * a.C + r] = -1;
-        }
-    }
 }
 
 size_t lds_bytes(int E, int R, bool with_table) {
@@ -343,7 +362,7 @@ size_t layout_workspace_bytes(int T, int E, int R) {
 
 hipError_t launch_layout(const int32_t* idx, int32_t* cnt_e, int32_t* cnt_r, int32_t* off_e, int32_t* off_r,
                          int32_t* pos, int32_t* recv_src, int32_t* flags, void* workspace, int T, int E, int k,
-                         int R, int C, hipStream_t stream) {
+                         int R, int C, int A, hipStream_t stream) {
     const int NB = (T + kTokensPerLayoutBlock - 1) / kTokensPerLayoutBlock;
     LayoutArgs a{};
     a.idx = idx;
@@ -359,6 +378,7 @@ hipError_t launch_layout(const int32_t* idx, int32_t* cnt_e, int32_t* cnt_r, int
     a.k = k;
     a.R = R;
     a.C = C;
+    a.A = A;
     a.NB = NB > 0 ? NB : 1;
     int32_t* ws = (int32_t*)workspace;
     a.ws_cnt = ws;

@@ -68,7 +68,7 @@ using namespace cgl;
 
 extern "C" {
 
-int32_t moe_abi_version(void) { return 1; }
+int32_t moe_abi_version(void) { return 2; }
 
 const char* moe_last_error(void) { return g_err; }
 
@@ -119,6 +119,11 @@ static moe_status check_layout_cfg(const moe_layout_cfg* c) {
     if (k < 1 || k > 64) return fail(MOE_ERR_INVALID, "layout: topk %d outside [1, 64]", k);
     if (R < 1 || R > E || E % R) return fail(MOE_ERR_INVALID, "layout: num_ranks %d must divide E", R);
     if (C < 0) return fail(MOE_ERR_INVALID, "layout: capacity %d < 0", C);
+    const int A = c->align_rows;
+    if (A < 0 || A > 4096) return fail(MOE_ERR_INVALID, "layout: align_rows %d outside [0, 4096]", A);
+    if (A > 1 && C > 0) return fail(MOE_ERR_INVALID, "layout: align_rows needs the compact layout (capacity 0)");
+    if (A > 1 && (int64_t)T * k + (int64_t)E * (A - 1) >= (1ll << 31))
+        return fail(MOE_ERR_INVALID, "layout: T*k + E*(align_rows-1) too large");
     if ((int64_t)T * k >= (1ll << 31)) return fail(MOE_ERR_INVALID, "layout: T*k too large");
     if ((int64_t)E * C >= (1ll << 31)) return fail(MOE_ERR_INVALID, "layout: E*C too large");
     return MOE_OK;
@@ -138,7 +143,8 @@ moe_status moe_get_layout(const moe_layout_cfg* c, const int32_t* topk_idx, int3
     if (!cnt_e || !cnt_r || !off_e || !off_r || !flags)
         return fail(MOE_ERR_INVALID, "layout: NULL output array");
     if (T > 0 && (!topk_idx || !pos)) return fail(MOE_ERR_INVALID, "layout: NULL topk_idx or pos");
-    const int64_t N = c->capacity > 0 ? (int64_t)c->num_experts * c->capacity : (int64_t)T * c->topk;
+    const int64_t N = c->capacity > 0 ? (int64_t)c->num_experts * c->capacity
+                      : (int64_t)T * c->topk + (c->align_rows > 1 ? (int64_t)c->num_experts * (c->align_rows - 1) : 0);
     if (N > 0 && !recv_src) return fail(MOE_ERR_INVALID, "layout: NULL recv_src");
     const void* ptrs[] = {topk_idx, cnt_e, cnt_r, off_e, off_r, pos, recv_src, flags};
     for (const void* p : ptrs)
@@ -149,7 +155,8 @@ moe_status moe_get_layout(const moe_layout_cfg* c, const int32_t* topk_idx, int3
                     workspace ? workspace_bytes : (size_t)0);
     if (!aligned(workspace, 16)) return fail(MOE_ERR_INVALID, "layout: workspace must be 16-byte aligned");
     return hip_status(launch_layout(topk_idx, cnt_e, cnt_r, off_e, off_r, pos, recv_src, flags, workspace, T,
-                                    c->num_experts, c->topk, c->num_ranks, c->capacity, (hipStream_t)stream),
+                                    c->num_experts, c->topk, c->num_ranks, c->capacity, c->align_rows,
+                                    (hipStream_t)stream),
                       "layout launch");
 }
 
@@ -159,7 +166,7 @@ moe_status moe_dispatch(const moe_dispatch_cfg* c, const uint16_t* x, const int3
     const int T = c->num_tokens, H = c->hidden, k = c->topk, N = c->num_recv_rows;
     if (T < 0 || N < 0) return fail(MOE_ERR_INVALID, "dispatch: negative size");
     if (k < 1 || k > 64) return fail(MOE_ERR_INVALID, "dispatch: topk %d outside [1, 64]", k);
-    const bool fp8 = c->dtype == MOE_DISPATCH_FP8_E4M3;
+    const bool fp8 = c->dtype == MOE_DISPATCH_FP8_E4M3 || c->dtype == MOE_DISPATCH_FP8_E4M3_POW2;
     if (!fp8 && c->dtype != MOE_DISPATCH_BF16) return fail(MOE_ERR_INVALID, "dispatch: unknown dtype %d", c->dtype);
     if (H < 1 || (fp8 && H % 128) || (!fp8 && H % 8))
         return fail(MOE_ERR_INVALID, "dispatch: hidden %d must be a positive multiple of %d", H, fp8 ? 128 : 8);
@@ -172,7 +179,7 @@ moe_status moe_dispatch(const moe_dispatch_cfg* c, const uint16_t* x, const int3
     if (!aligned(x, 16) || !aligned(recv_x, 16) || !aligned(pos, 4) || !aligned(recv_scales, 4))
         return fail(MOE_ERR_INVALID, "dispatch: x/recv_x must be 16-byte aligned, pos/scales 4-byte");
     if (N == 0) return ok();
-    return hip_status(launch_dispatch(x, pos, recv_x, recv_scales, T, H, k, N, fp8, upw, (hipStream_t)stream),
+    return hip_status(launch_dispatch(x, pos, recv_x, recv_scales, T, H, k, N, c->dtype, upw, (hipStream_t)stream),
                       "dispatch launch");
 }
 

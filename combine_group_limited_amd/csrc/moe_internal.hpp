@@ -14,12 +14,13 @@ size_t layout_workspace_bytes(int T, int E, int R);
 size_t layout_lds_bytes_host(int E, int R);
 hipError_t launch_layout(const int32_t* idx, int32_t* cnt_e, int32_t* cnt_r, int32_t* off_e, int32_t* off_r,
                          int32_t* pos, int32_t* recv_src, int32_t* flags, void* workspace, int T, int E,
-                         int k, int R, int C, hipStream_t stream);
+                         int k, int R, int C, int A, hipStream_t stream);
 
 // upw: 512-channel units per wave (0 = the library's choice for the shape)
 int dispatch_units_per_wave(int T, int H);
+// dtype: 0 FP8 (amax/448 scales), 1 BF16, 2 FP8 with power-of-two scales
 hipError_t launch_dispatch(const uint16_t* x, const int32_t* pos, void* recv_x, float* recv_scales, int T,
-                           int H, int k, int N, bool fp8, int upw, hipStream_t stream);
+                           int H, int k, int N, int dtype, int upw, hipStream_t stream);
 
 int combine_units_per_wave(int T, int H);
 hipError_t launch_combine(const uint16_t* y, const int32_t* pos, const float* w, uint16_t* out, int T, int H,

@@ -53,7 +53,11 @@ typedef enum {
 } moe_status;
 
 typedef enum { MOE_SCORE_SIGMOID = 0, MOE_SCORE_SOFTMAX = 1 } moe_score_fn;
-typedef enum { MOE_DISPATCH_FP8_E4M3 = 0, MOE_DISPATCH_BF16 = 1 } moe_dispatch_dtype;
+typedef enum {
+    MOE_DISPATCH_FP8_E4M3 = 0,      /* fp32 scale = amax / 448 per 128 channels */
+    MOE_DISPATCH_BF16 = 1,          /* verbatim copy */
+    MOE_DISPATCH_FP8_E4M3_POW2 = 2  /* power-of-two scale per 128 channels */
+} moe_dispatch_dtype;
 
 /* Bits of the *flags word written by moe_get_layout. */
 #define MOE_FLAG_CAPACITY_OVERFLOW 1  /* padded mode: some expert got more than C pairs */
@@ -125,6 +129,11 @@ moe_status moe_route_topk(const moe_route_cfg* cfg, const float* logits, int32_t
 /*       compact (capacity 0): off_e[e] + #{t' < t routed to e}; N = T*k    */
 /*       padded  (capacity C): e*C + #{t' < t routed to e}, or -1 when that */
 /*                is >= C (dropped; MOE_FLAG_CAPACITY_OVERFLOW); N = E*C    */
+/*       aligned (capacity 0, align_rows A > 1): every expert region starts  */
+/*                on a multiple of A rows: off_e is the exclusive scan of    */
+/*                cnt_e rounded up to A, pos = off_e[e] + rank; N = T*k +    */
+/*                E*(A-1) rows (an upper bound; off_e[E] rows are used).     */
+/*                A grouped-GEMM-friendly variant of the receive layout.     */
 /*   recv_src[p] = t*k + j for p = pos[t,j]; -1 for empty padded rows       */
 /*                                                           int32 [N]      */
 /*   flags[0]   = MOE_FLAG_* bits (0 = all good)             int32 [1]      */
@@ -141,6 +150,7 @@ typedef struct {
     int32_t topk;         /* k */
     int32_t num_ranks;    /* R */
     int32_t capacity;     /* 0 = compact; C > 0 = padded slots per expert */
+    int32_t align_rows;   /* compact only: 0 or 1 = packed; A > 1 = regions start on multiples of A */
 } moe_layout_cfg;
 
 size_t moe_layout_workspace_bytes(const moe_layout_cfg* cfg);
@@ -164,14 +174,17 @@ moe_status moe_get_layout(const moe_layout_cfg* cfg, const int32_t* topk_idx, in
 /*    recv_x[p, 128b+i] = E4M3FN nearest-even of the fp32 product           */
 /*    x[t,128b+i]*inv (OCP E4M3FN: max 448, sign kept), recv_scales[p,b] =  */
 /*    scale.  Dequantise as code * scale.                                    */
+/*  FP8_E4M3_POW2: as FP8_E4M3 but scale = 2^e, the smallest power of two   */
+/*    with a <= 448 * 2^e, and codes of the exactly scaled x * 2^-e (scales  */
+/*    that a GEMM can apply as exponent shifts).                            */
 /*  BF16: recv_x[p, :] = x[t, :] bit for bit.                               */
 /* Rows no pair addresses are not written.  pos of -1 (dropped) is skipped. */
 /*                                                                          */
 /* x           bf16 [T, H]                in                                */
 /* pos         int32 [T, k]               in (from moe_get_layout)          */
 /* recv_x      uint8 [N, H] (FP8) or bf16 [N, H]                 out        */
-/* recv_scales fp32 [N, H/128] (FP8; NULL for BF16)               out        */
-/* Limits: H % 128 == 0 (FP8) or H % 8 == 0 (BF16); 1 <= k <= 64.           */
+/* recv_scales fp32 [N, H/128] (FP8 dtypes; NULL for BF16)        out        */
+/* Limits: H % 128 == 0 (FP8 dtypes) or H % 8 == 0 (BF16); 1 <= k <= 64.    */
 /* ------------------------------------------------------------------------ */
 typedef struct {
     int32_t num_tokens;     /* T */

@@ -59,7 +59,7 @@ def lib():
         L.orc_route.restype = i32
         L.orc_route.argtypes = [i32] * 8 + [P, P, P]
         L.orc_layout.restype = i32
-        L.orc_layout.argtypes = [i32] * 5 + [P] * 8
+        L.orc_layout.argtypes = [i32] * 6 + [P] * 8
         L.orc_dispatch.restype = i32
         L.orc_dispatch.argtypes = [i32] * 5 + [P] * 4
         L.orc_combine.restype = i32
@@ -126,19 +126,19 @@ def route(logits: np.ndarray, num_groups: int, topk_group: int, topk: int,
     return idx, w
 
 
-def layout(idx: np.ndarray, num_experts: int, num_ranks: int, capacity: int = 0):
+def layout(idx: np.ndarray, num_experts: int, num_ranks: int, capacity: int = 0, align: int = 0):
     """Returns a dict with cnt_e, cnt_r, off_e, off_r, pos, recv_src, flags."""
     idx = np.ascontiguousarray(idx, dtype=np.int32)
     T, k = idx.shape
     E, R = num_experts, num_ranks
-    N = E * capacity if capacity > 0 else T * k
+    N = E * capacity if capacity > 0 else T * k + (E * (align - 1) if align > 1 else 0)
     out = dict(
         cnt_e=np.zeros(E, np.int32), cnt_r=np.zeros(R, np.int32),
         off_e=np.zeros(E + 1, np.int32), off_r=np.zeros(R + 1, np.int32),
         pos=np.zeros((T, k), np.int32), recv_src=np.zeros(N, np.int32),
         flags=np.zeros(1, np.int32),
     )
-    rc = lib().orc_layout(T, E, k, R, capacity, _p(idx), _p(out["cnt_e"]), _p(out["cnt_r"]),
+    rc = lib().orc_layout(T, E, k, R, capacity, align, _p(idx), _p(out["cnt_e"]), _p(out["cnt_r"]),
                           _p(out["off_e"]), _p(out["off_r"]), _p(out["pos"]),
                           _p(out["recv_src"]), _p(out["flags"]))
     if rc != 0:
@@ -147,7 +147,7 @@ def layout(idx: np.ndarray, num_experts: int, num_ranks: int, capacity: int = 0)
     return out
 
 
-FP8, BF16 = 0, 1
+FP8, BF16, FP8_POW2 = 0, 1, 2
 
 
 def dispatch(x_bits: np.ndarray, pos: np.ndarray, num_recv_rows: int, dtype: int = FP8,
@@ -162,8 +162,8 @@ def dispatch(x_bits: np.ndarray, pos: np.ndarray, num_recv_rows: int, dtype: int
     k = pos.shape[1]
     N = num_recv_rows
     if recv_x is None:
-        recv_x = np.zeros((N, H), dtype=np.uint8 if dtype == FP8 else np.uint16)
-    if dtype == FP8 and recv_scales is None:
+        recv_x = np.zeros((N, H), dtype=np.uint16 if dtype == BF16 else np.uint8)
+    if dtype != BF16 and recv_scales is None:
         recv_scales = np.zeros((N, H // 128), dtype=np.float32)
     sc = _p(recv_scales) if recv_scales is not None else None
     rc = lib().orc_dispatch(T, H, k, N, dtype, _p(x_bits), _p(pos), _p(recv_x), sc)

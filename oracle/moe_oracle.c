@@ -292,13 +292,15 @@ int orc_route(int T, int E, int G, int g, int k, int group_topn, int score_fn,
 /* rows keep recv_src -1.  Bit 1 of *flags marks an expert index outside     */
 /* [0,E) or repeated inside one token (the outputs are then unspecified).    */
 /* ------------------------------------------------------------------------ */
-int orc_layout(int T, int E, int k, int R, int C, const int32_t* idx,
+int orc_layout(int T, int E, int k, int R, int C, int A, const int32_t* idx,
                int32_t* cnt_e, int32_t* cnt_r, int32_t* off_e, int32_t* off_r,
                int32_t* pos, int32_t* recv_src, int32_t* flags)
 {
-    if (T < 0 || E <= 0 || k < 1 || R <= 0 || E % R != 0 || C < 0) return -1;
+    if (T < 0 || E <= 0 || k < 1 || R <= 0 || E % R != 0 || C < 0 || A < 0) return -1;
+    if (A > 1 && C > 0) return -1;
     const int Er = E / R;
-    const int64_t N = (C > 0) ? (int64_t)E * C : (int64_t)T * k;
+    const int64_t N = (C > 0) ? (int64_t)E * C
+                              : (int64_t)T * k + (A > 1 ? (int64_t)E * (A - 1) : 0);
     *flags = 0;
 
     for (int t = 0; t < T; ++t)
@@ -324,11 +326,18 @@ int orc_layout(int T, int E, int k, int R, int C, const int32_t* idx,
     }
     free(hit);
 
+    /* Reading for the aligned variant (the pages mention a GEMM-friendly
+       receive layout without describing it): every expert region starts on a
+       multiple of A rows. */
     off_e[0] = 0;
-    for (int e = 0; e < E; ++e) off_e[e + 1] = off_e[e] + cnt_e[e];
+    for (int e = 0; e < E; ++e) {
+        int span = cnt_e[e];
+        if (A > 1) span = (span + A - 1) / A * A;
+        off_e[e + 1] = off_e[e] + span;
+    }
     for (int r = 0; r <= R; ++r) off_r[r] = off_e[r * Er];
 
-    if (C > 0)
+    if (C > 0 || A > 1)
         for (int64_t i = 0; i < N; ++i) recv_src[i] = -1;
 
     int32_t* seen = (int32_t*)calloc((size_t)E, sizeof(int32_t));
@@ -376,7 +385,7 @@ int orc_dispatch(int T, int H, int k, int N, int dtype, const uint16_t* x,
             }
         return 0;
     }
-    if (dtype != 0 || H % 128 != 0) return -1;
+    if ((dtype != 0 && dtype != 2) || H % 128 != 0) return -1;
     const int S = H / 128;
     uint8_t* out = (uint8_t*)recv_x;
     uint8_t q[128];
@@ -389,11 +398,21 @@ int orc_dispatch(int T, int H, int k, int N, int dtype, const uint16_t* x,
                 if (v > amax) amax = v;
             }
             const float a = (amax > 0x1.0p-100f) ? amax : 0x1.0p-100f;
-            const float scale = a / 448.0f;
-            const float inv = 448.0f / a;
-            for (int i = 0; i < 128; ++i) {
-                const float prod = bf16_to_f32(xb[i]) * inv;
-                q[i] = orc_e4m3_from_f32(prod);
+            float scale;
+            if (dtype == 0) {
+                scale = a / 448.0f;
+                const float inv = 448.0f / a;
+                for (int i = 0; i < 128; ++i) {
+                    const float prod = bf16_to_f32(xb[i]) * inv;
+                    q[i] = orc_e4m3_from_f32(prod);
+                }
+            } else {
+                /* smallest power of two 2^e with a <= 448 * 2^e */
+                int e = ilogbf(a) - 9;
+                while (ldexp(448.0, e) < (double)a) ++e;
+                scale = ldexpf(1.0f, e);
+                for (int i = 0; i < 128; ++i)
+                    q[i] = orc_e4m3_from_f32(ldexpf(bf16_to_f32(xb[i]), -e));
             }
             for (int j = 0; j < k; ++j) {
                 const int p = pos[(size_t)t * k + j];

@@ -60,14 +60,19 @@ int orc_route(int T, int E, int G, int g, int k, int group_topn, int score_fn,
 
 /* capacity C = 0: compact receive buffer, N = T*k rows.
    capacity C > 0: padded, N = E*C rows, expert e owns rows [e*C, e*C + C).
+   align A > 1 (compact only): each expert's region starts at a multiple of A
+   rows (off_e = scan of counts rounded up to A); N = T*k + E*(A-1) rows, the
+   rows no pair fills hold recv_src -1.
    Outputs: cnt_e[E], cnt_r[R], off_e[E+1], off_r[R+1], pos[T,k], recv_src[N],
    overflow[1]. */
-int orc_layout(int T, int E, int k, int R, int C, const int32_t* idx,
+int orc_layout(int T, int E, int k, int R, int C, int A, const int32_t* idx,
                int32_t* cnt_e, int32_t* cnt_r, int32_t* off_e, int32_t* off_r,
                int32_t* pos, int32_t* recv_src, int32_t* overflow);
 
 /* dtype 0: FP8 E4M3FN with one fp32 scale per 128 channels (recv_x bytes [N,H],
-   recv_scales [N,H/128]); dtype 1: BF16 copy (recv_x as uint16 [N,H]).
+   recv_scales [N,H/128]); dtype 1: BF16 copy (recv_x as uint16 [N,H]);
+   dtype 2: FP8 E4M3FN with power-of-two scales (the smallest 2^e with
+   amax <= 448 * 2^e; codes of x / 2^e, exact scaling).
    Rows whose pos is -1 are skipped; rows never addressed are left untouched. */
 int orc_dispatch(int T, int H, int k, int N, int dtype, const uint16_t* x,
                  const int32_t* pos, void* recv_x, float* recv_scales);

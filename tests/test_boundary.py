@@ -37,7 +37,7 @@ def test_no_undefined_symbols_beyond_runtime():
 
 def test_status_strings_and_version():
     L = moe.lib()
-    assert L.moe_abi_version() == 1
+    assert L.moe_abi_version() == 2
     for s in (0, 1, 2, 4, 5):
         assert L.moe_status_string(s)
 
@@ -77,7 +77,8 @@ def test_layout_workspace_and_rejects():
     ok = moe.LayoutCfg(4096, 256, 8, 32, 0)
     assert L.moe_layout_workspace_bytes(ctypes.byref(ok)) >= 4 * 16 * (256 + 32 + 1)
     for vals in [(4, 256, 8, 33, 0), (4, 256, 0, 32, 0), (4, 256, 8, 32, -1), (-1, 256, 8, 32, 0),
-                 (4, 600, 8, 8, 0), (4, 256, 8, 512, 0)]:
+                 (4, 600, 8, 8, 0), (4, 256, 8, 512, 0), (4, 256, 8, 32, 0, -1),
+                 (4, 256, 8, 32, 4, 64), (4, 256, 8, 32, 0, 5000)]:
         cfg = moe.LayoutCfg(*vals)
         assert L.moe_layout_workspace_bytes(ctypes.byref(cfg)) == 0
         st = L.moe_get_layout(ctypes.byref(cfg), *([None] * 9), 0, None)

@@ -391,3 +391,39 @@ def test_stream_ordering_on_side_stream():
     torch.cuda.current_stream().wait_stream(s)
     assert np.array_equal(idx.cpu().numpy(), ref_i)
     assert np.array_equal(lay.cnt_e.cpu().numpy(), np.bincount(ref_i.ravel(), minlength=wl.E))
+
+
+# --------------------------------------------------------------------------
+# grouped-GEMM-friendly variants: aligned expert regions, power-of-two scales
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("name,T,A", [("dsv3_prefill", 4096, 128), ("dsv3_prefill", 4096, 64),
+                                      ("dsv3_prefill", 200, 8), ("mixtral", 16384, 256), ("tiny", 64, 4)])
+def test_layout_aligned_parity(name, T, A):
+    wl = W.get(name).replace(T=T)
+    say(f"[gpu] aligned layout {name} T={T} A={A}")
+    idx, _ = oracle.route(W.gen_logits(wl), wl.G, wl.g, wl.k, score_fn=sf(wl))
+    ref = oracle.layout(idx, wl.E, wl.R, align=A)
+    lay = moe.get_layout(torch.from_numpy(idx).to(DEV), wl.E, wl.R, align_rows=A)
+    for n in ("cnt_e", "cnt_r", "off_e", "off_r", "pos", "recv_src"):
+        assert np.array_equal(getattr(lay, n).cpu().numpy(), ref[n]), n
+    assert int(lay.flags.item()) == 0
+
+
+@pytest.mark.parametrize("name", ["dsv3_prefill", "tiny", "skewed_8k"])
+def test_dispatch_pow2_parity(name):
+    wl = W.get(name)
+    say(f"[gpu] pow2 dispatch {name}")
+    x = W.gen_x(wl)
+    x[0] = 0
+    x[1, :128] = W.f32_to_bf16_bits(np.full(128, 448.0, np.float32))
+    x[2, :128] = W.f32_to_bf16_bits(np.full(128, 450.0, np.float32))
+    x[3] = W.f32_to_bf16_bits(W.bf16_bits_to_f32(x[3]) * np.float32(3e38 / 5))
+    x[4] = W.f32_to_bf16_bits(W.bf16_bits_to_f32(x[4]) * np.float32(1e-38))
+    idx, _ = oracle.route(W.gen_logits(wl), wl.G, wl.g, wl.k)
+    lay = oracle.layout(idx, wl.E, wl.R, wl.capacity)
+    ref_q, ref_s = oracle.dispatch(x, lay["pos"], wl.N, oracle.FP8_POW2)
+    q, s = moe.dispatch(bf16_to_dev(x), torch.from_numpy(lay["pos"]).to(DEV), wl.N, "fp8_pow2",
+                        torch.zeros((wl.N, wl.H), dtype=torch.uint8, device=DEV),
+                        torch.zeros((wl.N, wl.S), dtype=torch.float32, device=DEV))
+    assert np.array_equal(q.cpu().numpy(), ref_q)
+    assert np.array_equal(s.cpu().numpy().view(np.uint32), ref_s.view(np.uint32))

@@ -698,3 +698,54 @@ def test_backward_dropped_pairs(orc):
     assert gw[0, 1] == 0.0
     gx = orc.dispatch_backward(y, pos)
     assert np.array_equal(gx[0], y[pos[0, 0]])
+
+
+# --------------------------------------------------------------------------
+# grouped-GEMM-friendly variants: tile-aligned regions, power-of-two scales
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("A", [1, 8, 64, 128])
+def test_layout_aligned_regions(orc, A):
+    rng = np.random.default_rng(A)
+    T, E, k, R = 200, 32, 4, 4
+    idx = _random_idx(rng, T, E, k, skew=True)
+    L = orc.layout(idx, E, R, align=A)
+    cnt = np.bincount(idx.ravel(), minlength=E)
+    assert np.array_equal(L["cnt_e"], cnt)
+    span = -(-cnt // A) * A if A > 1 else cnt
+    assert np.array_equal(np.diff(L["off_e"]), span)
+    assert np.all(L["off_e"] % max(A, 1) == 0)
+    N = T * k + (E * (A - 1) if A > 1 else 0)
+    assert L["recv_src"].shape == (N,)
+    order = np.argsort(idx.ravel(), kind="stable")
+    off = np.concatenate([[0], np.cumsum(cnt)])
+    ref = np.full(N, -1, np.int32)
+    for e in range(E):
+        ref[L["off_e"][e]:L["off_e"][e] + cnt[e]] = order[off[e]:off[e + 1]]
+    assert np.array_equal(L["recv_src"], ref)
+    assert np.array_equal(L["recv_src"][L["pos"].ravel()], np.arange(T * k))
+    if A == 1:
+        assert np.array_equal(L["pos"], orc.layout(idx, E, R)["pos"])
+
+
+def test_dispatch_pow2_scales(orc):
+    torch = pytest.importorskip("torch")
+    wl = _dsv3_small(T=64, H=1024)
+    x = W.gen_x(wl)
+    x[3, :128] = 0
+    x[5, 128:256] = W.f32_to_bf16_bits(np.full(128, 448.0, np.float32))   # amax exactly 448
+    x[6, 256:384] = W.f32_to_bf16_bits(np.full(128, 450.0, np.float32))   # next bf16 above
+    pos = np.arange(wl.T, dtype=np.int32)[:, None]
+    q, sc = orc.dispatch(x, pos, wl.T, dtype=orc.FP8_POW2)
+    m, e = np.frexp(sc.astype(np.float64))
+    assert np.all(m == 0.5)                                   # powers of two
+    xf = W.bf16_bits_to_f32(x).astype(np.float64).reshape(wl.T, wl.S, 128)
+    amax = np.maximum(np.abs(xf).max(2), 2.0 ** -100)
+    ratio = amax / sc
+    assert np.all((ratio <= 448) & (ratio > 224))             # the smallest such power
+    assert sc[5, 1] == 1.0 and sc[6, 2] == 2.0
+    # codes are the e4m3 rounding of the exactly scaled values (library check)
+    ref = torch.from_numpy((xf / sc[:, :, None]).astype(np.float32)).to(torch.float8_e4m3fn)
+    assert np.array_equal(q, ref.view(torch.uint8).numpy().reshape(wl.T, wl.H))
+    vals = np.array([orc.e4m3_value(c) for c in range(256)])
+    deq = vals[q].reshape(wl.T, wl.S, 128) * sc.astype(np.float64)[:, :, None]
+    assert np.all(np.abs(xf - deq) <= 2 ** -4 * np.abs(xf) + 2 ** -10 * sc[:, :, None])
