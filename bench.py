@@ -9,7 +9,10 @@ is not on this path: the combine reads synthetic expert outputs y [T*k, H].
 Inputs sit in HBM before the timed region; two input sets alternate between
 steps so no input is re-read from the 256 MB last-level cache.  Before the
 timed region the GPU is held by a short spin kernel while all K steps are
-enqueued, so the timeline holds only GPU work.  HIP events on the launch
+enqueued, so the timeline holds only GPU work.  A third pass of K steps, each
+preceded by a 1 GiB scratch read, reports the same stages with cold caches.
+For batches of at most 1024 tokens a fourth pass times the step with route,
+layout and dispatch in one launch (moe_route_dispatch).  HIP events on the launch
 stream (created without the system-scope fence) bracket every stage of every
 timed step; a second pass of K steps without them gives the step time free of
 their cost.
@@ -287,6 +290,21 @@ def main():
     torch.cuda.synchronize()
     ms_step_plain = hev.ms(start2, end2) / K
 
+    # cold-cache pass: before every step, outside its stage events, a 1 GiB
+    # scratch read evicts everything from the L2s and the 256 MB last-level
+    # cache (a read, not a write, so no dirty flush lines are left behind for
+    # the step's own stores to write back)
+    flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    flush_sum = torch.empty((), dtype=torch.float32, device=dev)
+    evs_cold = [hev.create(5) for _ in range(K)]
+    torch.cuda.synchronize()
+    for i in range(K):
+        torch.sum(flush, out=flush_sum)
+        step(i, evs_cold[i])
+    torch.cuda.synchronize()
+    del flush
+    cold = np.array([[hev.ms(e[q], e[q + 1]) for q in range(4)] for e in evs_cold]) * 1e3  # us
+
     ms_step = hev.ms(start, end) / K
     stage = np.array([[hev.ms(e[q], e[q + 1]) for q in range(4)] for e in evs])  # ms
     st_mean = stage.mean(0) * 1e3   # us
@@ -337,9 +355,63 @@ def main():
         "ms_per_step_without_stage_events": round(ms_step_plain, 4),
         "p10_p90_dispatch_plus_combine_us": [round(float(v), 2) for v in np.percentile(
             (stage[:, 2] + stage[:, 3]) * 1e3, [10, 90])],
+        "median_dispatch_plus_combine_us": round(float(np.median(stage[:, 2] + stage[:, 3])) * 1e3, 2),
         "wall_s_timed_region": round(t_wall, 4),
         "roofline": roof,
+        "cold_cache": {
+            "dispatch_us": round(float(cold[:, 2].mean()), 2),
+            "combine_us": round(float(cold[:, 3].mean()), 2),
+            "dispatch_plus_combine_us": round(float((cold[:, 2] + cold[:, 3]).mean()), 2),
+            "median_dispatch_plus_combine_us": round(float(np.median(cold[:, 2] + cold[:, 3])), 2),
+            "p10_p90_dispatch_plus_combine_us": [round(float(v), 2) for v in np.percentile(
+                cold[:, 2] + cold[:, 3], [10, 90])],
+            "gbps": round(dc_bytes / (float((cold[:, 2] + cold[:, 3]).mean()) * 1e-6) / 1e9, 1),
+            "route_us": round(float(cold[:, 0].mean()), 2),
+            "layout_us": round(float(cold[:, 1].mean()), 2),
+            "note": "each step preceded by a 1 GiB scratch read outside its events",
+        },
     }
+
+    # decode-sized batches: the same step with route + layout + dispatch in one
+    # launch (moe_route_dispatch), then the combine
+    if wl.T <= 1024:
+        try:
+            f_out = (idx, wts, lay_out[0], recv_x, recv_s)
+
+            def fstep(i, ev=None):
+                x, logits, y = sets[i % 2]
+                if ev: hev.record(ev[0], stream)
+                moe.route_dispatch(logits, x, wl.G, wl.g, wl.k, wl.R, wl.capacity, wl.dtype, wl.score,
+                                   out=f_out)
+                if ev: hev.record(ev[1], stream)
+                moe.combine(y, lay_out[0].pos, wts, out)
+                if ev: hev.record(ev[2], stream)
+
+            for i in range(args.warmup):
+                fstep(i)
+            fevs = [hev.create(3) for _ in range(K)]
+            torch.cuda.synchronize()
+            if hasattr(torch.cuda, "_sleep"):
+                torch.cuda._sleep(int(2e7))
+            for i in range(K):
+                fstep(i, fevs[i])
+            fs, fe = hev.create(2)
+            if hasattr(torch.cuda, "_sleep"):
+                torch.cuda._sleep(int(2e7))
+            hev.record(fs, stream)
+            for i in range(K):
+                fstep(i)
+            hev.record(fe, stream)
+            torch.cuda.synchronize()
+            fst = np.array([[hev.ms(e[q], e[q + 1]) for q in range(2)] for e in fevs]) * 1e3
+            res["one_launch_decode"] = {
+                "route_layout_dispatch_us": round(float(fst[:, 0].mean()), 2),
+                "combine_us": round(float(fst[:, 1].mean()), 2),
+                "ms_per_step_without_stage_events": round(hev.ms(fs, fe) / K, 4),
+                "separate_route_layout_dispatch_us": round(route_us + layout_us + disp_us, 2),
+            }
+        except moe.MoeError as e:
+            res["one_launch_decode"] = {"unsupported": str(e)}
 
     if args.copy_calibration:
         n = 1 << 30

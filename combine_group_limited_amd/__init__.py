@@ -1,7 +1,8 @@
 """MI355X-native MoE dispatch/combine: thin Python binding of ``libcgl_moe.so``.
 
 The four calls of the C ABI in ``include/moe.h`` -- ``route_topk``,
-``get_layout``, ``dispatch``, ``combine`` -- plus ``quantize_e4m3``.  This
+``get_layout``, ``dispatch``, ``combine`` -- the backward pair, the one-launch
+decode path ``route_dispatch``, and ``quantize_e4m3``.  This
 module only marshals arguments: it checks tensor shapes, dtypes and devices,
 allocates outputs with torch (device memory and the current stream are all
 torch provides here) and passes raw pointers to the library.  Every step of
@@ -72,8 +73,12 @@ def lib() -> ctypes.CDLL:
         L.moe_quantize_e4m3.argtypes = [P, P, ctypes.c_int64, P]
         L.moe_dispatch_backward.argtypes = [ctypes.POINTER(CombineCfg), P, P, P, P]
         L.moe_combine_backward.argtypes = [ctypes.POINTER(CombineCfg), P, P, P, P, P, P, P]
+        L.moe_route_dispatch_workspace_bytes.argtypes = []
+        L.moe_route_dispatch_workspace_bytes.restype = S
+        L.moe_route_dispatch.argtypes = ([ctypes.POINTER(RouteCfg), ctypes.POINTER(LayoutCfg),
+                                          ctypes.POINTER(DispatchCfg)] + [P] * 13 + [P, S, P])
         for f in ("moe_route_topk", "moe_get_layout", "moe_dispatch", "moe_combine", "moe_quantize_e4m3",
-                  "moe_dispatch_backward", "moe_combine_backward"):
+                  "moe_dispatch_backward", "moe_combine_backward", "moe_route_dispatch"):
             getattr(L, f).restype = ctypes.c_int
         L.moe_status_string.argtypes = [ctypes.c_int]
         L.moe_status_string.restype = ctypes.c_char_p
@@ -217,6 +222,68 @@ def dispatch(x, pos, num_recv_rows: int, dtype: str = "fp8", recv_x=None, recv_s
     _check(lib().moe_dispatch(ctypes.byref(cfg), _ptr(x), _ptr(pos), _ptr(recv_x),
                               _ptr(recv_scales) if fp8 else None, _stream(x.device)))
     return recv_x, (recv_scales if fp8 else None)
+
+
+_route_dispatch_ws = {}
+
+
+def route_dispatch_workspace(device):
+    """A zeroed barrier workspace for route_dispatch (one per device is cached
+    and used by default; calls that may overlap on different streams need
+    their own)."""
+    torch = _torch()
+    n = lib().moe_route_dispatch_workspace_bytes()
+    return torch.zeros(n, dtype=torch.uint8, device=device)
+
+
+def route_dispatch(logits, x, num_groups: int, topk_group: int, topk: int, num_ranks: int,
+                   capacity: int = 0, dtype: str = "fp8", score_fn: str = "sigmoid",
+                   renormalize: bool = True, group_topn: int = 0, align_rows: int = 0,
+                   out=None, workspace=None):
+    """Route + layout + dispatch in one launch (small batches, T <= 1024).
+
+    logits fp32 [T,E], x bf16 [T,H] -> (idx, w, Layout, recv_x, recv_scales), the
+    same tensors route_topk, get_layout and dispatch return.  out = (idx, w,
+    Layout, recv_x, recv_scales) reuses buffers."""
+    torch = _torch()
+    _need(logits, "logits", torch.float32)
+    _need(x, "x", torch.bfloat16, device=logits.device)
+    T, E = logits.shape
+    H = x.shape[1]
+    if x.shape[0] != T:
+        raise ValueError("x must be [T, H] with the T of logits")
+    dev = logits.device
+    N = recv_rows(T, E, topk, capacity, align_rows)
+    fp8 = dtype in ("fp8", "fp8_pow2")
+    if out is None:
+        idx = torch.empty((T, topk), dtype=torch.int32, device=dev)
+        w = torch.empty((T, topk), dtype=torch.float32, device=dev)
+        lay = alloc_layout(T, E, topk, num_ranks, capacity, dev, align_rows)[0]
+        recv_x = torch.empty((N, H), dtype=torch.uint8 if fp8 else torch.bfloat16, device=dev)
+        recv_scales = torch.empty((N, H // 128), dtype=torch.float32, device=dev) if fp8 else None
+    else:
+        idx, w, lay, recv_x, recv_scales = out
+        _need(idx, "idx", torch.int32, (T, topk), dev)
+        _need(w, "w", torch.float32, (T, topk), dev)
+        _need(recv_x, "recv_x", torch.uint8 if fp8 else torch.bfloat16, (N, H), dev)
+        if fp8:
+            _need(recv_scales, "recv_scales", torch.float32, (N, H // 128), dev)
+        if lay.num_recv_rows != N:
+            raise ValueError("layout buffers were sized for another receive layout")
+    if workspace is None:
+        key = (dev.type, dev.index if dev.index is not None else torch.cuda.current_device())
+        if key not in _route_dispatch_ws:
+            _route_dispatch_ws[key] = route_dispatch_workspace(dev)
+        workspace = _route_dispatch_ws[key]
+    rc = RouteCfg(T, E, num_groups, topk_group, topk, group_topn, SCORE_FNS[score_fn], int(renormalize))
+    lc = LayoutCfg(T, E, topk, num_ranks, capacity, align_rows)
+    dc = DispatchCfg(T, H, topk, N, DISPATCH_DTYPES[dtype], 0)
+    _check(lib().moe_route_dispatch(
+        ctypes.byref(rc), ctypes.byref(lc), ctypes.byref(dc), _ptr(logits), _ptr(x), _ptr(idx), _ptr(w),
+        _ptr(lay.cnt_e), _ptr(lay.cnt_r), _ptr(lay.off_e), _ptr(lay.off_r), _ptr(lay.pos), _ptr(lay.recv_src),
+        _ptr(lay.flags), _ptr(recv_x), _ptr(recv_scales) if fp8 else None, _ptr(workspace), workspace.numel(),
+        _stream(dev)))
+    return idx, w, lay, recv_x, (recv_scales if fp8 else None)
 
 
 def combine(y, pos, topk_w, out=None, units_per_wave: int = 0):

@@ -31,6 +31,7 @@ constexpr int kUnit = 512;             // channels per wave-wide 16-byte load
 #define CGL_DISPATCH_LDS_CAP 0
 #endif
 constexpr int kDispatchThreads = CGL_DISPATCH_THREADS;  // waves per block = threads / 64
+constexpr long long kDrainWaves = 2048;
 
 // cache policy of the x reads and the receive-buffer writes (1 = streaming).
 // Measured on MI355X at 4096 x 7168 top-8: streaming loads with ordinary
@@ -42,14 +43,13 @@ constexpr int kDispatchThreads = CGL_DISPATCH_THREADS;  // waves per block = thr
 #define CGL_DISPATCH_STORE_NT 0
 #endif
 // 1: wait until a destination row's stores have completed before starting
-// the next row (fewer rows open at once across the chip)
+// the next row (fewer rows open at once across the chip) when the grid has
+// at least kDrainWaves waves; smaller grids leave every row in flight.
+// Measured on MI355X: 48.9 vs 52.6 us at 4096 tokens (4 096 waves), but
+// 4.6 vs 3.8 us at 128 tokens (1 792 waves).
 #ifndef CGL_DISPATCH_DRAIN
 #define CGL_DISPATCH_DRAIN 1
 #endif
-
-// s_waitcnt vmcnt(0) (expcnt and lgkmcnt left at their "no wait" maxima):
-// on CDNA the vector-memory counter also counts outstanding stores.
-constexpr int kWaitStores = 0x0F70;
 
 struct DispatchArgs {
     const uint16_t* x;
@@ -59,36 +59,11 @@ struct DispatchArgs {
     int T, H, k, N, S;
     int units;   // ceil(H / 512)
     int chunks;  // ceil(units / U): waves per token
+    int drain;   // wait for each row's stores before the next
 };
 
 __device__ __forceinline__ u32x4 load16(const uint16_t* p) {
     return load_stream<CGL_DISPATCH_LOAD_NT>((const u32x4*)p);
-}
-
-// absmax of the 8 bf16 values held by a lane, as a 15-bit magnitude pattern
-__device__ __forceinline__ uint32_t lane_absmax_bits(const u32x4& v) {
-    const uint32_t m0 = max(v.x & 0x7FFFu, (v.x >> 16) & 0x7FFFu);
-    const uint32_t m1 = max(v.y & 0x7FFFu, (v.y >> 16) & 0x7FFFu);
-    const uint32_t m2 = max(v.z & 0x7FFFu, (v.z >> 16) & 0x7FFFu);
-    const uint32_t m3 = max(v.w & 0x7FFFu, (v.w >> 16) & 0x7FFFu);
-    return max(max(m0, m1), max(m2, m3));
-}
-
-// Block scale.  POW2 = false: scale = a/448, inv = 448/a (IEEE divisions).
-// POW2 = true: scale = 2^e with e the smallest integer such that a <= 448*2^e;
-// writing a = m * 2^E (m in [1,2)) and 448 = 1.75 * 2^8 gives
-// e = E - 8 + (m > 1.75), read straight off a's bits, and inv = 2^-e exactly.
-template <bool POW2>
-__device__ __forceinline__ void block_scale(float aa, float& scale, float& inv) {
-    if constexpr (POW2) {
-        const uint32_t b = __float_as_uint(aa);
-        const int e = (int)(b >> 23) - 127 - 8 + ((b & 0x7FFFFFu) > 0x600000u ? 1 : 0);
-        scale = __uint_as_float((uint32_t)(e + 127) << 23);
-        inv = __uint_as_float((uint32_t)(127 - e) << 23);
-    } else {
-        scale = aa / 448.0f;
-        inv = 448.0f / aa;
-    }
 }
 
 template <int U, bool POW2>
@@ -115,15 +90,7 @@ __global__ __launch_bounds__(kDispatchThreads) void dispatch_fp8_kernel(Dispatch
     float scale[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        const uint32_t m = row16_max_u32(lane_absmax_bits(v[u]));
-        const float amax = __uint_as_float(m << 16);
-        const float aa = amax > 0x1p-100f ? amax : 0x1p-100f;
-        float inv;
-        block_scale<POW2>(aa, scale[u], inv);
-        code[u].x = pack_e4m3x4(bf16_lo(v[u].x) * inv, bf16_hi(v[u].x) * inv, bf16_lo(v[u].y) * inv,
-                                bf16_hi(v[u].y) * inv);
-        code[u].y = pack_e4m3x4(bf16_lo(v[u].z) * inv, bf16_hi(v[u].z) * inv, bf16_lo(v[u].w) * inv,
-                                bf16_hi(v[u].w) * inv);
+        code[u] = quantize_unit<POW2>(v[u], scale[u]);
     }
 
     uint8_t* rx = (uint8_t*)a.recv_x;
@@ -140,7 +107,7 @@ __global__ __launch_bounds__(kDispatchThreads) void dispatch_fp8_kernel(Dispatch
                 if ((lane & 15) == 0) sdst[c >> 7] = scale[u];
             }
         }
-        if (CGL_DISPATCH_DRAIN) __builtin_amdgcn_s_waitcnt(kWaitStores);
+        if (CGL_DISPATCH_DRAIN && a.drain) __builtin_amdgcn_s_waitcnt(kWaitStores);
     }
 }
 
@@ -169,7 +136,7 @@ __global__ __launch_bounds__(kDispatchThreads) void dispatch_bf16_kernel(Dispatc
             const int c = (u0 + u) * kUnit + lane * 8;
             if (c < a.H) store_stream<CGL_DISPATCH_STORE_NT>(v[u], (u32x4*)(dst + c));
         }
-        if (CGL_DISPATCH_DRAIN) __builtin_amdgcn_s_waitcnt(kWaitStores);
+        if (CGL_DISPATCH_DRAIN && a.drain) __builtin_amdgcn_s_waitcnt(kWaitStores);
     }
 }
 
@@ -177,6 +144,7 @@ template <int U>
 hipError_t launch_u(DispatchArgs a, int dtype, hipStream_t s) {
     a.chunks = (a.units + U - 1) / U;
     const long long waves = (long long)a.T * a.chunks;
+    a.drain = waves >= kDrainWaves ? 1 : 0;
     const int wpb = kDispatchThreads / kWave;
     const unsigned blocks = (unsigned)((waves + wpb - 1) / wpb);
     if (dtype == 0)

@@ -143,44 +143,6 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_count_kernel(LayoutArgs
     if (threadIdx.x == 0) a.ws_bad[b] = any_bad;
 }
 
-// Inclusive scan of one value per lane across a wave.
-__device__ __forceinline__ int wave_inclusive_scan(int v) {
-    const int lane = threadIdx.x & 63;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        const int o = __shfl_up(v, d, 64);
-        if (lane >= d) v += o;
-    }
-    return v;
-}
-
-// Exclusive scan of tot[0..E) (each rounded up to a multiple of A when A > 1)
-// into off[0..E] (off[E] = total), block-wide: each thread owns a run of
-// ceil(E/256) experts.
-__device__ void block_exclusive_scan(const int32_t* tot, int32_t* off, int E, int A) {
-    __shared__ int32_t wave_tot[kLayoutWaves];
-    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
-    const int per = (E + kLayoutThreads - 1) / kLayoutThreads;
-    const int lo = min(tid * per, E), hi = min(lo + per, E);
-    auto span = [A](int c) { return A > 1 ? (c + A - 1) / A * A : c; };
-    int s = 0;
-    for (int e = lo; e < hi; ++e) s += span(tot[e]);
-    const int inc = wave_inclusive_scan(s);
-    if (lane == 63) wave_tot[w] = inc;
-    __syncthreads();
-    int base = 0;
-#pragma unroll
-    for (int q = 0; q < kLayoutWaves; ++q)
-        if (q < w) base += wave_tot[q];
-    int run = base + inc - s;
-    for (int e = lo; e < hi; ++e) {
-        off[e] = run;
-        run += span(tot[e]);
-    }
-    if (tid == kLayoutThreads - 1) off[E] = run;
-    __syncthreads();
-}
-
 // Pass 2 (FUSED: the only block, counts taken from its own masks).
 template <int KT, bool FUSED>
 __global__ __launch_bounds__(kLayoutThreads) void layout_position_kernel(LayoutArgs a) {
@@ -254,7 +216,7 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_position_kernel(LayoutA
         }
     }
     __syncthreads();
-    block_exclusive_scan(tot, off, a.E, a.A);
+    block_exclusive_scan<kLayoutThreads>(tot, off, a.E, a.A);
 
     // ---- block 0 publishes counts, offsets and flags ----------------------
     if (b == 0) {

@@ -68,7 +68,7 @@ using namespace cgl;
 
 extern "C" {
 
-int32_t moe_abi_version(void) { return 2; }
+int32_t moe_abi_version(void) { return 3; }
 
 const char* moe_last_error(void) { return g_err; }
 
@@ -83,8 +83,8 @@ const char* moe_status_string(moe_status s) {
     return "unknown status";
 }
 
-moe_status moe_route_topk(const moe_route_cfg* c, const float* logits, int32_t* topk_idx, float* topk_w,
-                          void* stream) {
+// Validates a routing configuration; *n_out receives the group-score depth.
+static moe_status check_route_cfg(const moe_route_cfg* c, int* n_out) {
     if (!c) return fail(MOE_ERR_INVALID, "route: cfg is NULL");
     const int T = c->num_tokens, E = c->num_experts, G = c->num_groups, g = c->topk_group, k = c->topk;
     if (T < 0) return fail(MOE_ERR_INVALID, "route: num_tokens %d < 0", T);
@@ -102,12 +102,22 @@ moe_status moe_route_topk(const moe_route_cfg* c, const float* logits, int32_t* 
         return fail(MOE_ERR_INVALID, "route: unknown score_fn %d", c->score_fn);
     if (c->renormalize != 0 && c->renormalize != 1)
         return fail(MOE_ERR_INVALID, "route: renormalize must be 0 or 1");
+    *n_out = n;
+    return MOE_OK;
+}
+
+moe_status moe_route_topk(const moe_route_cfg* c, const float* logits, int32_t* topk_idx, float* topk_w,
+                          void* stream) {
+    int n = 0;
+    const moe_status st = check_route_cfg(c, &n);
+    if (st != MOE_OK) return st;
+    const int T = c->num_tokens;
     if (T == 0) return ok();
     if (!logits || !topk_idx || !topk_w) return fail(MOE_ERR_INVALID, "route: NULL array");
     if (!aligned(logits, 4) || !aligned(topk_idx, 4) || !aligned(topk_w, 4))
         return fail(MOE_ERR_INVALID, "route: arrays must be 4-byte aligned");
-    return hip_status(launch_route(logits, topk_idx, topk_w, T, E, G, g, k, n, c->score_fn, c->renormalize,
-                                   (hipStream_t)stream),
+    return hip_status(launch_route(logits, topk_idx, topk_w, T, c->num_experts, c->num_groups, c->topk_group,
+                                   c->topk, n, c->score_fn, c->renormalize, (hipStream_t)stream),
                       "route launch");
 }
 
@@ -160,8 +170,7 @@ moe_status moe_get_layout(const moe_layout_cfg* c, const int32_t* topk_idx, int3
                       "layout launch");
 }
 
-moe_status moe_dispatch(const moe_dispatch_cfg* c, const uint16_t* x, const int32_t* pos, void* recv_x,
-                        float* recv_scales, void* stream) {
+static moe_status check_dispatch_cfg(const moe_dispatch_cfg* c) {
     if (!c) return fail(MOE_ERR_INVALID, "dispatch: cfg is NULL");
     const int T = c->num_tokens, H = c->hidden, k = c->topk, N = c->num_recv_rows;
     if (T < 0 || N < 0) return fail(MOE_ERR_INVALID, "dispatch: negative size");
@@ -173,14 +182,76 @@ moe_status moe_dispatch(const moe_dispatch_cfg* c, const uint16_t* x, const int3
     const int upw = c->units_per_wave;
     if (!(upw == 0 || upw == 1 || upw == 2 || upw == 4 || upw == 7 || upw == 8 || upw == 14))
         return fail(MOE_ERR_INVALID, "dispatch: units_per_wave %d not in {0,1,2,4,7,8,14}", upw);
+    return MOE_OK;
+}
+
+moe_status moe_dispatch(const moe_dispatch_cfg* c, const uint16_t* x, const int32_t* pos, void* recv_x,
+                        float* recv_scales, void* stream) {
+    const moe_status st = check_dispatch_cfg(c);
+    if (st != MOE_OK) return st;
+    const int T = c->num_tokens, H = c->hidden, k = c->topk, N = c->num_recv_rows;
+    const bool fp8 = c->dtype != MOE_DISPATCH_BF16;
     if (T == 0) return ok();
     if (!x || !pos || (N > 0 && !recv_x) || (fp8 && N > 0 && !recv_scales))
         return fail(MOE_ERR_INVALID, "dispatch: NULL array");
     if (!aligned(x, 16) || !aligned(recv_x, 16) || !aligned(pos, 4) || !aligned(recv_scales, 4))
         return fail(MOE_ERR_INVALID, "dispatch: x/recv_x must be 16-byte aligned, pos/scales 4-byte");
     if (N == 0) return ok();
-    return hip_status(launch_dispatch(x, pos, recv_x, recv_scales, T, H, k, N, c->dtype, upw, (hipStream_t)stream),
+    return hip_status(launch_dispatch(x, pos, recv_x, recv_scales, T, H, k, N, c->dtype, c->units_per_wave,
+                                      (hipStream_t)stream),
                       "dispatch launch");
+}
+
+size_t moe_route_dispatch_workspace_bytes(void) { return 4096; }
+
+moe_status moe_route_dispatch(const moe_route_cfg* rc, const moe_layout_cfg* lc, const moe_dispatch_cfg* dc,
+                              const float* logits, const uint16_t* x, int32_t* topk_idx, float* topk_w,
+                              int32_t* cnt_e, int32_t* cnt_r, int32_t* off_e, int32_t* off_r, int32_t* pos,
+                              int32_t* recv_src, int32_t* flags, void* recv_x, float* recv_scales, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+    int n = 0;
+    moe_status st = check_route_cfg(rc, &n);
+    if (st != MOE_OK) return st;
+    if ((st = check_layout_cfg(lc)) != MOE_OK) return st;
+    if ((st = check_dispatch_cfg(dc)) != MOE_OK) return st;
+    const int T = rc->num_tokens, E = rc->num_experts, k = rc->topk, R = lc->num_ranks, C = lc->capacity;
+    const int A = lc->align_rows > 1 ? lc->align_rows : 0;
+    if (lc->num_tokens != T || dc->num_tokens != T)
+        return fail(MOE_ERR_INVALID, "route_dispatch: num_tokens differ (%d, %d, %d)", T, lc->num_tokens,
+                    dc->num_tokens);
+    if (lc->num_experts != E) return fail(MOE_ERR_INVALID, "route_dispatch: num_experts differ");
+    if (lc->topk != k || dc->topk != k) return fail(MOE_ERR_INVALID, "route_dispatch: topk differs");
+    const int64_t N = C > 0 ? (int64_t)E * C : (int64_t)T * k + (A > 1 ? (int64_t)E * (A - 1) : 0);
+    if (dc->num_recv_rows != N)
+        return fail(MOE_ERR_INVALID, "route_dispatch: num_recv_rows %d, the layout has %lld", dc->num_recv_rows,
+                    (long long)N);
+    if (dc->units_per_wave != 0) return fail(MOE_ERR_INVALID, "route_dispatch: units_per_wave must be 0");
+    if (T > kFusedMaxTokens)
+        return fail(MOE_ERR_UNSUPPORTED, "route_dispatch: num_tokens %d above %d", T, kFusedMaxTokens);
+    const size_t lds = fused_decode_lds_bytes(T, E, k, R);
+    if (lds > kFusedMaxLds)
+        return fail(MOE_ERR_UNSUPPORTED, "route_dispatch: shape needs %zu bytes of LDS, above %zu", lds,
+                    (size_t)kFusedMaxLds);
+    const bool fp8 = dc->dtype != MOE_DISPATCH_BF16;
+    if (!cnt_e || !cnt_r || !off_e || !off_r || !flags) return fail(MOE_ERR_INVALID, "route_dispatch: NULL array");
+    if (T > 0 && (!logits || !x || !topk_idx || !topk_w || !pos))
+        return fail(MOE_ERR_INVALID, "route_dispatch: NULL array");
+    if (N > 0 && (!recv_src || !recv_x || (fp8 && !recv_scales)))
+        return fail(MOE_ERR_INVALID, "route_dispatch: NULL receive array");
+    const void* p4[] = {logits, topk_idx, topk_w, cnt_e, cnt_r, off_e, off_r, pos, recv_src, flags, recv_scales};
+    for (const void* p : p4)
+        if (!aligned(p, 4)) return fail(MOE_ERR_INVALID, "route_dispatch: arrays must be 4-byte aligned");
+    if (!aligned(x, 16) || !aligned(recv_x, 16))
+        return fail(MOE_ERR_INVALID, "route_dispatch: x and recv_x must be 16-byte aligned");
+    if (!workspace || workspace_bytes < moe_route_dispatch_workspace_bytes())
+        return fail(MOE_ERR_WORKSPACE, "route_dispatch: workspace needs %zu bytes, got %zu",
+                    moe_route_dispatch_workspace_bytes(), workspace ? workspace_bytes : (size_t)0);
+    if (!aligned(workspace, 16)) return fail(MOE_ERR_INVALID, "route_dispatch: workspace must be 16-byte aligned");
+    return hip_status(launch_fused_decode(logits, x, topk_idx, topk_w, cnt_e, cnt_r, off_e, off_r, pos, recv_src,
+                                          flags, recv_x, recv_scales, (uint32_t*)workspace, T, E, rc->num_groups,
+                                          rc->topk_group, k, n, rc->score_fn, rc->renormalize, R, C, A, (int)N,
+                                          dc->hidden, dc->dtype, (hipStream_t)stream),
+                      "route_dispatch launch");
 }
 
 moe_status moe_combine(const moe_combine_cfg* c, const uint16_t* y, const int32_t* pos, const float* topk_w,

@@ -250,4 +250,94 @@ __device__ __forceinline__ uint32_t pack_e4m3x4(float a, float b, float c, float
     return (uint32_t)w;
 }
 
+
+// s_waitcnt vmcnt(0) (expcnt and lgkmcnt left at their "no wait" maxima):
+// on CDNA the vector-memory counter also counts outstanding stores.
+constexpr int kWaitStores = 0x0F70;
+
+// ---------------------------------------------------------------------------
+// FP8 quantisation of one 512-channel unit held as 8 bf16 per lane (lane l:
+// channels 8l..8l+7), so a 128-channel scale block is one 16-lane DPP row.
+// ---------------------------------------------------------------------------
+// absmax of the 8 bf16 values held by a lane, as a 15-bit magnitude pattern
+__device__ __forceinline__ uint32_t lane_absmax_bits(const u32x4& v) {
+    const uint32_t m0 = max(v.x & 0x7FFFu, (v.x >> 16) & 0x7FFFu);
+    const uint32_t m1 = max(v.y & 0x7FFFu, (v.y >> 16) & 0x7FFFu);
+    const uint32_t m2 = max(v.z & 0x7FFFu, (v.z >> 16) & 0x7FFFu);
+    const uint32_t m3 = max(v.w & 0x7FFFu, (v.w >> 16) & 0x7FFFu);
+    return max(max(m0, m1), max(m2, m3));
+}
+
+// Block scale of a 128-channel block with absmax aa (> 0).  POW2 = false: scale = a/448, inv = 448/a (IEEE divisions).
+// POW2 = true: scale = 2^e with e the smallest integer such that a <= 448*2^e;
+// writing a = m * 2^E (m in [1,2)) and 448 = 1.75 * 2^8 gives
+// e = E - 8 + (m > 1.75), read straight off a's bits, and inv = 2^-e exactly.
+template <bool POW2>
+__device__ __forceinline__ void block_scale(float aa, float& scale, float& inv) {
+    if constexpr (POW2) {
+        const uint32_t b = __float_as_uint(aa);
+        const int e = (int)(b >> 23) - 127 - 8 + ((b & 0x7FFFFFu) > 0x600000u ? 1 : 0);
+        scale = __uint_as_float((uint32_t)(e + 127) << 23);
+        inv = __uint_as_float((uint32_t)(127 - e) << 23);
+    } else {
+        scale = aa / 448.0f;
+        inv = 448.0f / aa;
+    }
+}
+
+// Codes (8 per lane, byte i = channel 8l+i) and the scale of the lane's
+// 128-channel block: amax floored at 2^-100, codes of x * inv.
+template <bool POW2>
+__device__ __forceinline__ u32x2 quantize_unit(const u32x4& v, float& scale) {
+    const uint32_t m = row16_max_u32(lane_absmax_bits(v));
+    const float amax = __uint_as_float(m << 16);
+    const float aa = amax > 0x1p-100f ? amax : 0x1p-100f;
+    float inv;
+    block_scale<POW2>(aa, scale, inv);
+    u32x2 code;
+    code.x = pack_e4m3x4(bf16_lo(v.x) * inv, bf16_hi(v.x) * inv, bf16_lo(v.y) * inv, bf16_hi(v.y) * inv);
+    code.y = pack_e4m3x4(bf16_lo(v.z) * inv, bf16_hi(v.z) * inv, bf16_lo(v.w) * inv, bf16_hi(v.w) * inv);
+    return code;
+}
+
+// Inclusive scan of one value per lane across a wave.
+__device__ __forceinline__ int wave_inclusive_scan(int v) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int o = __shfl_up(v, d, 64);
+        if (lane >= d) v += o;
+    }
+    return v;
+}
+
+// Exclusive scan of tot[0..E) (each rounded up to a multiple of A when A > 1)
+// into off[0..E] (off[E] = total), by a whole block of THREADS threads: each
+// thread owns a run of ceil(E/THREADS) experts.  Both arrays may be in LDS.
+template <int THREADS>
+__device__ void block_exclusive_scan(const int32_t* tot, int32_t* off, int E, int A) {
+    constexpr int kWaves = THREADS / kWave;
+    __shared__ int32_t wave_tot[kWaves];
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+    const int per = (E + THREADS - 1) / THREADS;
+    const int lo = min(tid * per, E), hi = min(lo + per, E);
+    auto span = [A](int c) { return A > 1 ? (c + A - 1) / A * A : c; };
+    int s = 0;
+    for (int e = lo; e < hi; ++e) s += span(tot[e]);
+    const int inc = wave_inclusive_scan(s);
+    if (lane == 63) wave_tot[w] = inc;
+    __syncthreads();
+    int base = 0;
+#pragma unroll
+    for (int q = 0; q < kWaves; ++q)
+        if (q < w) base += wave_tot[q];
+    int run = base + inc - s;
+    for (int e = lo; e < hi; ++e) {
+        off[e] = run;
+        run += span(tot[e]);
+    }
+    if (tid == THREADS - 1) off[E] = run;
+    __syncthreads();
+}
+
 }  // namespace cgl

@@ -30,6 +30,16 @@ hipError_t launch_combine_backward(const uint16_t* grad_out, const uint16_t* y, 
                                    uint16_t* grad_y, float* grad_w, int T, int H, int k, int N, int upw,
                                    hipStream_t stream);
 
+// Fused decode path (route + layout + dispatch in one launch), for small T.
+constexpr int kFusedMaxTokens = 1024;
+constexpr size_t kFusedMaxLds = 64512;  // 64 KiB of dynamic LDS less 1 KiB for static
+size_t fused_decode_lds_bytes(int T, int E, int k, int R);
+hipError_t launch_fused_decode(const float* logits, const uint16_t* x, int32_t* idx, float* w, int32_t* cnt_e,
+                               int32_t* cnt_r, int32_t* off_e, int32_t* off_r, int32_t* pos, int32_t* recv_src,
+                               int32_t* flags, void* recv_x, float* recv_scales, uint32_t* barrier, int T, int E,
+                               int G, int g, int k, int n, int score_fn, int renorm, int R, int C, int A, int N,
+                               int H, int dtype, hipStream_t stream);
+
 hipError_t launch_quantize_e4m3(const float* in, uint8_t* out, int64_t n, hipStream_t stream);
 
 }  // namespace cgl

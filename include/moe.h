@@ -259,6 +259,51 @@ moe_status moe_combine_backward(const moe_combine_cfg* cfg, const uint16_t* grad
                                 void* stream);
 
 /* ------------------------------------------------------------------------ */
+/* moe_route_dispatch -- decode path: route, layout and dispatch of a small  */
+/* batch in ONE kernel launch.                                              */
+/*                                                                          */
+/* Follows the DeepEP V2 digest (GeekNews 19438), section "training/prefill/*/
+/* decoding usage" (at decode, routing metadata should not cost a layout    */
+/* recomputation and a CPU synchronisation), and "DeepSeek, DeepEP          */
+/* open-sourced" (GeekNews 19421), "Performance > Low-latency kernels"      */
+/* (decode batches of 128 tokens per rank, judged by latency).             */
+/*                                                                          */
+/* Computes exactly what moe_route_topk(route) -> moe_get_layout(layout) -> */
+/* moe_dispatch(dispatch) compute, with every output of the three calls     */
+/* (bit for bit), in one launch whose blocks meet once at a grid-wide       */
+/* barrier after routing.  For inputs with MOE_FLAG_BAD_INDEX unset; on top */
+/* of moe_get_layout it also writes -1 to compact rows no pair fills.       */
+/* The three configurations must agree: the same num_tokens, num_experts    */
+/* and topk; dispatch num_recv_rows equal to the layout's N;               */
+/* dispatch units_per_wave 0.                                               */
+/*                                                                          */
+/* logits fp32 [T,E] and x bf16 [T,H] in; topk_idx, topk_w, cnt_e, cnt_r,   */
+/* off_e, off_r, pos, recv_src, flags, recv_x, recv_scales out, with the    */
+/* shapes and meanings of the three calls above.                            */
+/* workspace: at least moe_route_dispatch_workspace_bytes() of device       */
+/* memory, 16-byte aligned, ZEROED BEFORE ITS FIRST USE (e.g. hipMemset     */
+/* once).  It holds the barrier's arrival counters and generation flags;    */
+/* every call leaves the counters at zero, so it needs no clearing between  */
+/* calls.                                                                   */
+/* Calls that may run at the same time (different streams) need different   */
+/* workspaces.  Its third 32-bit word counts blocks that stopped waiting at */
+/* the barrier after about a second (which only happens if the GPU cannot   */
+/* hold the whole grid at once); it stays 0 in normal use, and the outputs  */
+/* of a call that raised it are incomplete.                                 */
+/* Limits: those of the three calls, and T <= 1024 with                     */
+/*   8*ceil(T/64)*(E+R) + 4*(2E + 1 + T*k + 2048) <= 64512 bytes of LDS;     */
+/*   larger shapes return MOE_ERR_UNSUPPORTED (use the three calls).        */
+/* ------------------------------------------------------------------------ */
+size_t moe_route_dispatch_workspace_bytes(void);
+
+moe_status moe_route_dispatch(const moe_route_cfg* route, const moe_layout_cfg* layout,
+                              const moe_dispatch_cfg* dispatch, const float* logits,
+                              const uint16_t* x, int32_t* topk_idx, float* topk_w, int32_t* cnt_e,
+                              int32_t* cnt_r, int32_t* off_e, int32_t* off_r, int32_t* pos,
+                              int32_t* recv_src, int32_t* flags, void* recv_x, float* recv_scales,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
 /* moe_quantize_e4m3 -- the element conversion moe_dispatch uses, exposed   */
 /* on its own: out[i] = E4M3FN nearest-even of in[i], magnitudes above 448  */
 /* saturate to 448, sign kept (codes for NaN inputs are unspecified).       */

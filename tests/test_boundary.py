@@ -37,7 +37,7 @@ def test_no_undefined_symbols_beyond_runtime():
 
 def test_status_strings_and_version():
     L = moe.lib()
-    assert L.moe_abi_version() == 2
+    assert L.moe_abi_version() == 3
     for s in (0, 1, 2, 4, 5):
         assert L.moe_status_string(s)
 
@@ -135,3 +135,45 @@ def test_binding_has_no_fallback(tmp_path, monkeypatch):
     monkeypatch.setattr(moe, "_lib", None)
     with pytest.raises(ImportError):
         moe.lib()
+
+
+def _route_dispatch(rc, lc, dc, ws_bytes=256, fake=None):
+    """Calls moe_route_dispatch with host-side configurations only; `fake` is
+    a non-NULL dummy pointer for the arrays (never dereferenced: every case
+    here fails validation before any launch)."""
+    L = moe.lib()
+    r, l, d = moe.RouteCfg(*rc), moe.LayoutCfg(*lc), moe.DispatchCfg(*dc)
+    p = fake
+    return L.moe_route_dispatch(ctypes.byref(r), ctypes.byref(l), ctypes.byref(d), p, p, p, p, p, p, p, p, p,
+                                p, p, p, p, p, ws_bytes, None)
+
+
+DECODE_RC = (128, 256, 8, 4, 8, 0, 0, 1)
+DECODE_LC = (128, 256, 8, 32, 128, 0)
+DECODE_DC = (128, 7168, 8, 256 * 128, 0, 0)
+
+
+def test_route_dispatch_workspace_size():
+    assert moe.lib().moe_route_dispatch_workspace_bytes() >= 12
+
+
+@pytest.mark.parametrize("rc,lc,dc,status", [
+    # configurations that disagree with each other
+    ((128, 256, 8, 4, 8, 0, 0, 1), (64, 256, 8, 32, 128, 0), DECODE_DC, moe.MOE_ERR_INVALID),
+    ((128, 256, 8, 4, 8, 0, 0, 1), (128, 128, 8, 32, 128, 0), DECODE_DC, moe.MOE_ERR_INVALID),
+    ((128, 256, 8, 4, 8, 0, 0, 1), (128, 256, 4, 32, 128, 0), DECODE_DC, moe.MOE_ERR_INVALID),
+    (DECODE_RC, DECODE_LC, (128, 7168, 8, 128 * 8, 0, 0), moe.MOE_ERR_INVALID),   # N of the compact layout
+    (DECODE_RC, DECODE_LC, (128, 7168, 8, 256 * 128, 0, 2), moe.MOE_ERR_INVALID),  # launch-shape override
+    (DECODE_RC, DECODE_LC, (128, 7000, 8, 256 * 128, 0, 0), moe.MOE_ERR_INVALID),  # H % 128 for FP8
+    ((128, 256, 8, 9, 8, 0, 0, 1), DECODE_LC, DECODE_DC, moe.MOE_ERR_INVALID),     # bad routing cfg
+    # valid but beyond the one-launch limits
+    ((2048, 256, 8, 4, 8, 0, 0, 1), (2048, 256, 8, 32, 0, 0), (2048, 7168, 8, 2048 * 8, 0, 0),
+     moe.MOE_ERR_UNSUPPORTED),
+    ((1024, 512, 8, 4, 32, 0, 0, 1), (1024, 512, 32, 512, 0, 0), (1024, 7168, 32, 1024 * 32, 0, 0),
+     moe.MOE_ERR_UNSUPPORTED),
+    # valid shape, NULL arrays
+    (DECODE_RC, DECODE_LC, DECODE_DC, moe.MOE_ERR_INVALID),
+])
+def test_route_dispatch_rejects(rc, lc, dc, status):
+    assert _route_dispatch(rc, lc, dc) == status
+    assert moe.lib().moe_last_error()
