@@ -9,7 +9,8 @@ Which passage each function follows is stated in ``moe_oracle.c``:
 route -- Perplexity "Efficient and Portable Mixture-of-Experts Communication",
 section "Introduction", and the GeekNews DeepEP digest (group-limited gating);
 layout/dispatch -- same Perplexity page, sections "Portable kernels" and
-"Dispatch"; combine -- section "Combine".
+"Dispatch"; combine -- section "Combine"; the expert MLP -- the Mega MoE news
+page and the TileKernels news page, "functions".
 """
 from __future__ import annotations
 
@@ -68,6 +69,10 @@ def lib():
         L.orc_dispatch_backward.argtypes = [i32] * 4 + [P] * 3
         L.orc_combine_backward.restype = i32
         L.orc_combine_backward.argtypes = [i32] * 4 + [P] * 6
+        for name in ("orc_mlp_up", "orc_mlp_down"):
+            getattr(L, name).restype = i32
+        L.orc_mlp_up.argtypes = [i32] * 4 + [P, P, i32] + [P] * 8
+        L.orc_mlp_down.argtypes = [i32] * 4 + [P, P, i32] + [P] * 6
         _lib = L
     return _lib
 
@@ -214,3 +219,51 @@ def combine_backward(grad_out_bits: np.ndarray, y_bits: np.ndarray, pos: np.ndar
     if lib().orc_combine_backward(T, H, k, N, _p(g), _p(y), _p(pos), _p(w), _p(grad_y), _p(grad_w)) != 0:
         raise ValueError("oracle combine_backward: invalid arguments")
     return grad_y, grad_w
+
+
+def _ranges(start, count):
+    return (np.ascontiguousarray(start, dtype=np.int32), np.ascontiguousarray(count, dtype=np.int32))
+
+
+def mlp_up(x, xs, w1, w1s, start, count, rows=None, act=None, act_s=None, want_f64=False):
+    """Expert up projection + SwiGLU + FP8 (power-of-two scale) quantisation.
+
+    x uint8 [N,H], xs f32 [N,H/128], w1 uint8 [E,2I,H], w1s f32 [E,2I/128,H/128];
+    start/count int32 [E].  Returns (act uint8 [N,I], act_s f32 [N,I/128],
+    act_f64 [N,I] or None); rows not computed keep the arrays passed in."""
+    x = np.ascontiguousarray(x, dtype=np.uint8)
+    xs = np.ascontiguousarray(xs, dtype=np.float32)
+    w1 = np.ascontiguousarray(w1, dtype=np.uint8)
+    w1s = np.ascontiguousarray(w1s, dtype=np.float32)
+    N, H = x.shape
+    E, I2, _ = w1.shape
+    I = I2 // 2
+    st, ct = _ranges(start, count)
+    act = np.zeros((N, I), np.uint8) if act is None else act
+    act_s = np.zeros((N, I // 128), np.float32) if act_s is None else act_s
+    f64 = np.full((N, I), np.nan) if want_f64 else None
+    r = None if rows is None else np.ascontiguousarray(rows, dtype=np.int32)
+    rc = lib().orc_mlp_up(N, H, I, E, _p(st), _p(ct), 0 if r is None else r.size,
+                          None if r is None else _p(r), _p(x), _p(xs), _p(w1), _p(w1s), _p(act),
+                          _p(act_s), None if f64 is None else _p(f64))
+    if rc != 0:
+        raise ValueError("oracle mlp_up: invalid arguments")
+    return act, act_s, f64
+
+
+def mlp_down(act, act_s, w2, w2s, start, count, rows=None, y=None):
+    """Expert down projection: y bf16 bits [N,H] = bf16(act @ w2[e]^T) per row."""
+    act = np.ascontiguousarray(act, dtype=np.uint8)
+    act_s = np.ascontiguousarray(act_s, dtype=np.float32)
+    w2 = np.ascontiguousarray(w2, dtype=np.uint8)
+    w2s = np.ascontiguousarray(w2s, dtype=np.float32)
+    N, I = act.shape
+    E, H, _ = w2.shape
+    st, ct = _ranges(start, count)
+    y = np.zeros((N, H), np.uint16) if y is None else y
+    r = None if rows is None else np.ascontiguousarray(rows, dtype=np.int32)
+    rc = lib().orc_mlp_down(N, H, I, E, _p(st), _p(ct), 0 if r is None else r.size,
+                            None if r is None else _p(r), _p(act), _p(act_s), _p(w2), _p(w2s), _p(y))
+    if rc != 0:
+        raise ValueError("oracle mlp_down: invalid arguments")
+    return y

@@ -369,6 +369,22 @@ int orc_layout(int T, int E, int k, int R, int C, int A, const int32_t* idx,
 /* rounded); code = nearest E4M3FN of the fp32 product x * inv; the scales   */
 /* are a separate row-aligned [N, H/128] fp32 tensor.                        */
 /* ------------------------------------------------------------------------ */
+/* One block of 128 fp32 values -> E4M3FN codes with a power-of-two scale:
+   a = max(max |v|, 2^-100); scale = 2^e, the smallest power of two with
+   a <= 448 * 2^e; code i = nearest E4M3FN of the exactly scaled v[i] * 2^-e.
+   Returns the scale. */
+static float quant_block_pow2(const float* v, uint8_t* q)
+{
+    float amax = 0.0f;
+    for (int i = 0; i < 128; ++i)
+        if (fabsf(v[i]) > amax) amax = fabsf(v[i]);
+    const float a = (amax > 0x1.0p-100f) ? amax : 0x1.0p-100f;
+    int e = ilogbf(a) - 9;
+    while (ldexp(448.0, e) < (double)a) ++e;
+    for (int i = 0; i < 128; ++i) q[i] = orc_e4m3_from_f32(ldexpf(v[i], -e));
+    return ldexpf(1.0f, e);
+}
+
 int orc_dispatch(int T, int H, int k, int N, int dtype, const uint16_t* x,
                  const int32_t* pos, void* recv_x, float* recv_scales)
 {
@@ -407,12 +423,9 @@ int orc_dispatch(int T, int H, int k, int N, int dtype, const uint16_t* x,
                     q[i] = orc_e4m3_from_f32(prod);
                 }
             } else {
-                /* smallest power of two 2^e with a <= 448 * 2^e */
-                int e = ilogbf(a) - 9;
-                while (ldexp(448.0, e) < (double)a) ++e;
-                scale = ldexpf(1.0f, e);
-                for (int i = 0; i < 128; ++i)
-                    q[i] = orc_e4m3_from_f32(ldexpf(bf16_to_f32(xb[i]), -e));
+                float v[128];
+                for (int i = 0; i < 128; ++i) v[i] = bf16_to_f32(xb[i]);
+                scale = quant_block_pow2(v, q);
             }
             for (int j = 0; j < k; ++j) {
                 const int p = pos[(size_t)t * k + j];
@@ -494,4 +507,126 @@ int orc_combine_backward(int T, int H, int k, int N, const uint16_t* grad_out,
             grad_w[(size_t)t * k + j] = (float)dot;
         }
     return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Expert MLP on the receive buffer: the two linear layers and the SwiGLU    */
+/* between dispatch and combine (Mega MoE news page: the MoE layer runs      */
+/* dispatch, a first linear layer, SwiGLU, a second linear layer and         */
+/* combine; TileKernels news page, "functions": SwiGLU fused with the FP8    */
+/* quantisation).  Operands are FP8 E4M3FN with power-of-two block scales:   */
+/* activations one scale per row and 128 columns, weights one per 128x128    */
+/* block.  Every product and sum is taken in double on the dequantised       */
+/* operands (code value times scale, exact), in index order.                 */
+/* ------------------------------------------------------------------------ */
+static int expert_of_row(int E, const int32_t* start, const int32_t* count, int p)
+{
+    for (int e = 0; e < E; ++e)
+        if (p >= start[e] && p < start[e] + count[e]) return e;
+    return -1;
+}
+
+/* Visits the rows to compute: the list if given, else every expert's range. */
+static int mlp_rows(int N, int E, const int32_t* start, const int32_t* count, int nrows,
+                    const int32_t* rows, int (*fn)(void*, int, int), void* ctx)
+{
+    if (rows) {
+        for (int i = 0; i < nrows; ++i) {
+            const int p = rows[i];
+            if (p < 0 || p >= N) return -1;
+            const int e = expert_of_row(E, start, count, p);
+            if (e < 0) return -1;
+            if (fn(ctx, p, e)) return -1;
+        }
+        return 0;
+    }
+    for (int e = 0; e < E; ++e) {
+        if (count[e] < 0 || start[e] < 0 || (int64_t)start[e] + count[e] > N) return -1;
+        for (int p = start[e]; p < start[e] + count[e]; ++p)
+            if (fn(ctx, p, e)) return -1;
+    }
+    return 0;
+}
+
+struct up_ctx {
+    int H, I;
+    const uint8_t *x, *w1;
+    const float *xs, *w1s;
+    uint8_t* act;
+    float* act_s;
+    double* act_f64;
+};
+
+static int up_row(void* vc, int p, int e)
+{
+    const struct up_ctx* c = (const struct up_ctx*)vc;
+    const int H = c->H, I = c->I, SH = H / 128, S2I = 2 * I / 128;
+    double* xv = (double*)malloc(sizeof(double) * H);
+    double* h = (double*)malloc(sizeof(double) * 2 * I);
+    float* a32 = (float*)malloc(sizeof(float) * I);
+    if (!xv || !h || !a32) { free(xv); free(h); free(a32); return -1; }
+    for (int k = 0; k < H; ++k)
+        xv[k] = orc_e4m3_value(c->x[(size_t)p * H + k]) * (double)c->xs[(size_t)p * SH + k / 128];
+    for (int n = 0; n < 2 * I; ++n) {
+        const uint8_t* wr = c->w1 + ((size_t)e * 2 * I + n) * H;
+        const float* ws = c->w1s + ((size_t)e * S2I + n / 128) * SH;
+        double acc = 0.0;
+        for (int k = 0; k < H; ++k) acc += xv[k] * (orc_e4m3_value(wr[k]) * (double)ws[k / 128]);
+        h[n] = acc;
+    }
+    for (int j = 0; j < I; ++j) {
+        const double g = h[j], u = h[I + j];
+        const double a = g / (1.0 + exp(-g)) * u;   /* SwiGLU: silu(gate) * up */
+        if (c->act_f64) c->act_f64[(size_t)p * I + j] = a;
+        a32[j] = (float)a;
+    }
+    for (int b = 0; b < I / 128; ++b)
+        c->act_s[(size_t)p * (I / 128) + b] =
+            quant_block_pow2(a32 + (size_t)b * 128, c->act + (size_t)p * I + (size_t)b * 128);
+    free(xv); free(h); free(a32);
+    return 0;
+}
+
+int orc_mlp_up(int N, int H, int I, int E, const int32_t* start, const int32_t* count, int nrows,
+               const int32_t* rows, const uint8_t* x, const float* xs, const uint8_t* w1,
+               const float* w1s, uint8_t* act, float* act_s, double* act_f64)
+{
+    if (N < 0 || H <= 0 || I <= 0 || E < 1 || H % 128 || I % 128) return -1;
+    struct up_ctx c = {H, I, x, w1, xs, w1s, act, act_s, act_f64};
+    return mlp_rows(N, E, start, count, nrows, rows, up_row, &c);
+}
+
+struct down_ctx {
+    int H, I;
+    const uint8_t *act, *w2;
+    const float *as, *w2s;
+    uint16_t* y;
+};
+
+static int down_row(void* vc, int p, int e)
+{
+    const struct down_ctx* c = (const struct down_ctx*)vc;
+    const int H = c->H, I = c->I, SI = I / 128;
+    double* av = (double*)malloc(sizeof(double) * I);
+    if (!av) return -1;
+    for (int k = 0; k < I; ++k)
+        av[k] = orc_e4m3_value(c->act[(size_t)p * I + k]) * (double)c->as[(size_t)p * SI + k / 128];
+    for (int n = 0; n < H; ++n) {
+        const uint8_t* wr = c->w2 + ((size_t)e * H + n) * I;
+        const float* ws = c->w2s + ((size_t)e * (H / 128) + n / 128) * SI;
+        double acc = 0.0;
+        for (int k = 0; k < I; ++k) acc += av[k] * (orc_e4m3_value(wr[k]) * (double)ws[k / 128]);
+        c->y[(size_t)p * H + n] = orc_bf16_from_f64(acc);
+    }
+    free(av);
+    return 0;
+}
+
+int orc_mlp_down(int N, int H, int I, int E, const int32_t* start, const int32_t* count, int nrows,
+                 const int32_t* rows, const uint8_t* act, const float* act_s, const uint8_t* w2,
+                 const float* w2s, uint16_t* y)
+{
+    if (N < 0 || H <= 0 || I <= 0 || E < 1 || H % 128 || I % 128) return -1;
+    struct down_ctx c = {H, I, act, w2, act_s, w2s, y};
+    return mlp_rows(N, E, start, count, nrows, rows, down_row, &c);
 }

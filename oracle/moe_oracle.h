@@ -95,6 +95,26 @@ int orc_combine_backward(int T, int H, int k, int N, const uint16_t* grad_out,
                          const uint16_t* y, const int32_t* pos, const float* w,
                          uint16_t* grad_y, float* grad_w);
 
+/* Expert MLP (between dispatch and combine).  Expert e owns receive rows
+   [start[e], start[e] + count[e]).  rows: the rows to compute (nrows of them,
+   each inside some expert's range), or NULL for every row of every expert.
+   Operands: x codes [N,H] with power-of-two scales xs [N,H/128]; w1 codes
+   [E,2I,H] with scales w1s [E,2I/128,H/128] (rows 0..I-1 gate, I..2I-1 up);
+   act codes [N,I] with scales [N,I/128]; w2 codes [E,H,I] with scales
+   [E,H/128,I/128]; y bf16 [N,H].
+   up:   h[p,n] = sum_k x(p,k) w1(e,n,k)  (double, dequantised operands);
+         act[p,j] = silu(h[p,j]) * h[p,I+j], silu(g) = g/(1+exp(-g))  (double);
+         then rounded to fp32 and quantised per 128 columns (power-of-two scale,
+         as dispatch's FP8_E4M3_POW2); act_f64 (optional) receives the doubles.
+   down: y[p,n] = bf16( sum_k act(p,k) w2(e,n,k) )  (double, one rounding).
+   Rows not computed are left untouched. */
+int orc_mlp_up(int N, int H, int I, int E, const int32_t* start, const int32_t* count, int nrows,
+               const int32_t* rows, const uint8_t* x, const float* xs, const uint8_t* w1,
+               const float* w1s, uint8_t* act, float* act_s, double* act_f64);
+int orc_mlp_down(int N, int H, int I, int E, const int32_t* start, const int32_t* count, int nrows,
+                 const int32_t* rows, const uint8_t* act, const float* act_s, const uint8_t* w2,
+                 const float* w2s, uint16_t* y);
+
 #ifdef __cplusplus
 }
 #endif

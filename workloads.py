@@ -19,6 +19,12 @@ The shapes are the pages' workloads:
 DeepSeek-V3 uses 256 routed experts in 8 groups; the pages give 4096 x 7168
 top-8 with top-4 groups, the expert and group counts are the model's.
 
+Expert-MLP workloads (the step between dispatch and combine; Mega MoE news
+page): FP8 E4M3FN operands with power-of-two block scales drawn directly as
+bit patterns (sign, exponent field and mantissa uniform over a range), never
+by quantising real numbers, and per-expert row counts drawn multinomially.
+The expert width I is not on the pages: 2048 (DeepSeek-V3's) is our choice.
+
 Recipe: numpy ``default_rng(seed)`` streams; x ~ N(0,1) and y ~ N(0,1) drawn
 in fp32 and rounded to bf16 (nearest-even on the bit pattern); router logits
 ~ N(0,1) fp32.  Sub-streams: x = seed, logits = seed+1, y = seed+2, Zipf
@@ -167,3 +173,74 @@ def describe(wl: Workload) -> str:
 __all__ = ["Workload", "WORKLOADS", "get", "gen_x", "gen_logits", "gen_y", "tie_heavy",
            "f32_to_bf16_bits", "bf16_bits_to_f32", "zipf_bias", "algorithmic_bytes",
            "describe", "SKEW_BETA", "custom"]
+
+
+# --------------------------------------------------------------------------
+# expert MLP inputs
+# --------------------------------------------------------------------------
+@dataclasses.dataclass(frozen=True)
+class MlpWorkload:
+    name: str
+    N: int          # receive rows
+    H: int          # hidden size
+    I: int          # expert intermediate size
+    E: int          # experts whose rows are in the buffer
+    align: int = 0  # expert regions start on multiples of this many rows (0: packed)
+    seed: int = 0
+
+    def replace(self, **kw) -> "MlpWorkload":
+        return dataclasses.replace(self, **kw)
+
+
+MLP_WORKLOADS = {
+    "mlp_tiny": MlpWorkload("mlp_tiny", N=300, H=256, I=256, E=3),
+    # one rank of a 32-rank expert-parallel DeepSeek-V3 layer: 8 local experts
+    # receive 32 ranks x 4096 tokens x top-8 / 32 = 32768 rows
+    "mlp_rank": MlpWorkload("mlp_rank", N=32768, H=7168, I=2048, E=8),
+    # the single-GPU receive buffer of dsv3_prefill: 256 experts, 32768 rows
+    "mlp_all": MlpWorkload("mlp_all", N=32768, H=7168, I=2048, E=256),
+}
+
+
+def mlp_ranges(wl: MlpWorkload):
+    """Per-expert row counts (multinomial, seed+10) and region starts: (start,
+    count, rows_needed) int32; with align > 1 each start is a multiple of align."""
+    rng = np.random.default_rng(wl.seed + 10)
+    A = wl.align if wl.align > 1 else 1
+    total = wl.N - (wl.E * (A - 1) if A > 1 else 0)
+    count = rng.multinomial(total, np.full(wl.E, 1.0 / wl.E)).astype(np.int32)
+    span = (count + A - 1) // A * A
+    start = np.concatenate([[0], np.cumsum(span)[:-1]]).astype(np.int32)
+    return start, count, int(start[-1] + span[-1])
+
+
+def _fp8_codes(rng, shape, emin: int, emax: int) -> np.ndarray:
+    """Random E4M3FN bit patterns: sign, exponent field in [emin, emax] and
+    mantissa uniform; the NaN pattern (exponent 15, mantissa 7) is avoided."""
+    sign = rng.integers(0, 2, shape, dtype=np.uint8)
+    ex = rng.integers(emin, emax + 1, shape, dtype=np.uint8)
+    man = rng.integers(0, 8, shape, dtype=np.uint8)
+    man = np.where((ex == 15) & (man == 7), np.uint8(6), man)
+    return ((sign << 7) | (ex << 3) | man).astype(np.uint8)
+
+
+def _pow2(rng, shape, lo: int, hi: int) -> np.ndarray:
+    return np.ldexp(np.float32(1.0), rng.integers(lo, hi + 1, shape)).astype(np.float32)
+
+
+def gen_mlp_x(wl: MlpWorkload):
+    """FP8 activations [N,H] and power-of-two scales [N,H/128] (values up to ~1.75)."""
+    rng = np.random.default_rng(wl.seed + 11)
+    return _fp8_codes(rng, (wl.N, wl.H), 8, 15), _pow2(rng, (wl.N, wl.H // 128), -9, -8)
+
+
+def gen_mlp_weights(wl: MlpWorkload, which: str):
+    """'w1': codes [E,2I,H], scales [E,2I/128,H/128]; 'w2': codes [E,H,I], scales
+    [E,H/128,I/128].  Magnitudes keep the projections of order one."""
+    if which == "w1":
+        rng = np.random.default_rng(wl.seed + 12)
+        R, K = 2 * wl.I, wl.H
+    else:
+        rng = np.random.default_rng(wl.seed + 13)
+        R, K = wl.H, wl.I
+    return _fp8_codes(rng, (wl.E, R, K), 4, 9), _pow2(rng, (wl.E, R // 128, K // 128), -8, -7)
