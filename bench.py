@@ -50,6 +50,9 @@ def parse():
     ap.add_argument("--cpu-reps", type=int, default=0, help="oracle repetitions (0: about 10 s)")
     ap.add_argument("--direction", choices=["forward", "backward"], default="forward",
                     help="backward: time combine_backward -> dispatch_backward instead")
+    ap.add_argument("--stage", choices=["dispatch_combine", "mlp"], default="dispatch_combine",
+                    help="mlp: time the expert MLP (up + SwiGLU + FP8 requantisation, down) instead")
+    ap.add_argument("--mlp-workload", default="mlp_rank", choices=sorted(W.MLP_WORKLOADS))
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also time a plain 1 GiB device copy (reference for counters and peak)")
     return ap.parse_args()
@@ -203,6 +206,96 @@ def backward_main(args, wl, moe, torch, dev, sets, hev, stream):
     print(json.dumps(res), flush=True)
 
 
+FP8_MFMA_PEAK_TFLOPS = 5000.0   # MI355X dense FP8 matrix peak, published
+
+
+def mlp_cpu_baseline(wl, x, xs, w1, w1s, w2, w2s, start, count, rows: int = 4):
+    """The oracle's expert MLP on a sample of rows (plain single-threaded C)."""
+    import oracle
+    sel = np.array([start[e] + count[e] // 2 for e in range(min(rows, wl.E)) if count[e] > 0], np.int32)
+    t0 = time.perf_counter()
+    act, act_s, _ = oracle.mlp_up(x, xs, w1, w1s, start, count, rows=sel)
+    oracle.mlp_down(act, act_s, w2, w2s, start, count, rows=sel)
+    dt = time.perf_counter() - t0
+    flops = 2.0 * len(sel) * (2 * wl.I * wl.H + wl.H * wl.I)
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+            "sample": f"{len(sel)} receive rows (one per expert) through the oracle's up and down "
+                      f"projections, {dt:.1f} s, single thread"}
+
+
+def mlp_main(args, torch, moe, hev, dev):
+    """The expert MLP between dispatch and combine on one rank's receive
+    buffer: moe_expert_up (first layer, SwiGLU, FP8 requantisation) then
+    moe_expert_down (second layer to bf16)."""
+    wl = W.MLP_WORKLOADS[args.mlp_workload]
+    start, count, _ = W.mlp_ranges(wl)
+    xh, xsh = W.gen_mlp_x(wl)
+    w1h, w1sh = W.gen_mlp_weights(wl, "w1")
+    w2h, w2sh = W.gen_mlp_weights(wl, "w2")
+    d = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    x, xs, w1, w1s, w2, w2s = map(d, (xh, xsh, w1h, w1sh, w2h, w2sh))
+    off = np.zeros(wl.E + 1, np.int32)
+    off[:wl.E] = start
+    off[wl.E] = start[-1] + count[-1]
+    cnt, off_d = d(count.astype(np.int32)), d(off)
+    act = torch.empty((wl.N, wl.I), dtype=torch.uint8, device=dev)
+    act_s = torch.empty((wl.N, wl.I // 128), dtype=torch.float32, device=dev)
+    y = torch.empty((wl.N, wl.H), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+
+    def step(ev=None):
+        if ev: hev.record(ev[0], stream)
+        moe.expert_up(x, xs, w1, w1s, cnt, off_d, 0, act, act_s)
+        if ev: hev.record(ev[1], stream)
+        moe.expert_down(act, act_s, w2, w2s, cnt, off_d, 0, y)
+        if ev: hev.record(ev[2], stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    K = args.steps
+    evs = [hev.create(3) for _ in range(K)]
+    start_ev, end_ev = hev.create(2)
+    if hasattr(torch.cuda, "_sleep"):
+        torch.cuda._sleep(int(2e7))
+    hev.record(start_ev, stream)
+    for i in range(K):
+        step(evs[i])
+    hev.record(end_ev, stream)
+    torch.cuda.synchronize()
+    st = np.array([[hev.ms(e[q], e[q + 1]) for q in range(2)] for e in evs]) * 1e3
+    up_us, down_us = (float(v) for v in st.mean(0))
+    rows = int(count.sum())
+    f_up = 2.0 * rows * 2 * wl.I * wl.H
+    f_down = 2.0 * rows * wl.H * wl.I
+    tf_up = f_up / (up_us * 1e-6) / 1e12
+    tf_down = f_down / (down_us * 1e-6) / 1e12
+    value = (f_up + f_down) / ((up_us + down_us) * 1e-6) / 1e12
+    dom = "up" if up_us >= down_us else "down"
+    ach = tf_up if dom == "up" else tf_down
+    digest = source_digest("mlp.hip", "moe_device.hpp")
+    res = {
+        "metric": "expert MLP TFLOP/s (FP8 up + SwiGLU + FP8 requantisation, FP8 down to bf16)",
+        "value": round(value, 1), "unit": "TFLOP/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
+        "ms_per_step": round(hev.ms(start_ev, end_ev) / K, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "fp8 e4m3 (fp32 accumulate)",
+        "data": "synthetic FP8 codes with power-of-two block scales, multinomial rows per expert",
+        "config": {"workload": f"{wl.name}: N={wl.N} H={wl.H} I={wl.I} E={wl.E}", "rows": rows,
+                   "parallelism": "single GPU"},
+        "up_us": round(up_us, 1), "down_us": round(down_us, 1),
+        "up_tflops": round(tf_up, 1), "down_tflops": round(tf_down, 1),
+        "roofline": {"kernel": f"mlp_kernel<{'true' if dom == 'up' else 'false'}> ({dom})", "bound": "mfma",
+                     "achieved": round(ach, 1), "peak": FP8_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(ach / FP8_MFMA_PEAK_TFLOPS, 4),
+                     "traffic": load_traffic("mlp_" + dom, digest),
+                     "algorithmic_flops": f_up if dom == "up" else f_down,
+                     "avg_launch_us": round(up_us if dom == "up" else down_us, 1), "source_digest": digest},
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = mlp_cpu_baseline(wl, xh, xsh, w1h, w1sh, w2h, w2sh, start, count)
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -215,6 +308,8 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.stage == "mlp":
+        return mlp_main(args, torch, moe, HipEvents(), dev)
     wl = W.get(args.workload)
     fp8 = wl.dtype == "fp8"
 

@@ -2,7 +2,8 @@
 
 The four calls of the C ABI in ``include/moe.h`` -- ``route_topk``,
 ``get_layout``, ``dispatch``, ``combine`` -- the backward pair, the one-launch
-decode path ``route_dispatch``, and ``quantize_e4m3``.  This
+decode path ``route_dispatch``, the expert MLP ``expert_up`` / ``expert_down``,
+and ``quantize_e4m3``.  This
 module only marshals arguments: it checks tensor shapes, dtypes and devices,
 allocates outputs with torch (device memory and the current stream are all
 torch provides here) and passes raw pointers to the library.  Every step of
@@ -46,6 +47,11 @@ class DispatchCfg(ctypes.Structure):
         "num_tokens", "hidden", "topk", "num_recv_rows", "dtype", "units_per_wave")]
 
 
+class MlpCfg(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "num_rows", "hidden", "inter", "num_experts", "capacity")]
+
+
 class CombineCfg(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "num_tokens", "hidden", "topk", "num_recv_rows", "units_per_wave")]
@@ -77,8 +83,11 @@ def lib() -> ctypes.CDLL:
         L.moe_route_dispatch_workspace_bytes.restype = S
         L.moe_route_dispatch.argtypes = ([ctypes.POINTER(RouteCfg), ctypes.POINTER(LayoutCfg),
                                           ctypes.POINTER(DispatchCfg)] + [P] * 13 + [P, S, P])
+        L.moe_expert_up.argtypes = [ctypes.POINTER(MlpCfg)] + [P] * 9
+        L.moe_expert_down.argtypes = [ctypes.POINTER(MlpCfg)] + [P] * 8
         for f in ("moe_route_topk", "moe_get_layout", "moe_dispatch", "moe_combine", "moe_quantize_e4m3",
-                  "moe_dispatch_backward", "moe_combine_backward", "moe_route_dispatch"):
+                  "moe_dispatch_backward", "moe_combine_backward", "moe_route_dispatch", "moe_expert_up",
+                  "moe_expert_down"):
             getattr(L, f).restype = ctypes.c_int
         L.moe_status_string.argtypes = [ctypes.c_int]
         L.moe_status_string.restype = ctypes.c_char_p
@@ -284,6 +293,63 @@ def route_dispatch(logits, x, num_groups: int, topk_group: int, topk: int, num_r
         _ptr(lay.flags), _ptr(recv_x), _ptr(recv_scales) if fp8 else None, _ptr(workspace), workspace.numel(),
         _stream(dev)))
     return idx, w, lay, recv_x, (recv_scales if fp8 else None)
+
+
+def expert_up(x, x_scales, w1, w1_scales, cnt_e, off_e, capacity: int = 0, act=None, act_scales=None):
+    """First expert layer + SwiGLU + FP8 requantisation.  x uint8 [N,H] with
+    power-of-two scales fp32 [N,H/128]; w1 uint8 [E,2I,H], w1_scales fp32
+    [E,2I/128,H/128]; cnt_e/off_e from get_layout -> (act uint8 [N,I],
+    act_scales fp32 [N,I/128])."""
+    torch = _torch()
+    _need(x, "x", torch.uint8)
+    dev = x.device
+    N, H = x.shape
+    E, I2, H2 = w1.shape
+    I = I2 // 2
+    if H2 != H:
+        raise ValueError("w1 must be [E, 2I, H]")
+    _need(x_scales, "x_scales", torch.float32, (N, H // 128), dev)
+    _need(w1, "w1", torch.uint8, device=dev)
+    _need(w1_scales, "w1_scales", torch.float32, (E, I2 // 128, H // 128), dev)
+    _need(cnt_e, "cnt_e", torch.int32, (E,), dev)
+    if capacity == 0:
+        _need(off_e, "off_e", torch.int32, (E + 1,), dev)
+    if act is None:
+        act = torch.empty((N, I), dtype=torch.uint8, device=dev)
+        act_scales = torch.empty((N, I // 128), dtype=torch.float32, device=dev)
+    else:
+        _need(act, "act", torch.uint8, (N, I), dev)
+        _need(act_scales, "act_scales", torch.float32, (N, I // 128), dev)
+    cfg = MlpCfg(N, H, I, E, capacity)
+    _check(lib().moe_expert_up(ctypes.byref(cfg), _ptr(cnt_e), _ptr(off_e), _ptr(x), _ptr(x_scales), _ptr(w1),
+                               _ptr(w1_scales), _ptr(act), _ptr(act_scales), _stream(dev)))
+    return act, act_scales
+
+
+def expert_down(act, act_scales, w2, w2_scales, cnt_e, off_e, capacity: int = 0, y=None):
+    """Second expert layer: act uint8 [N,I] (power-of-two scales [N,I/128]),
+    w2 uint8 [E,H,I], w2_scales [E,H/128,I/128] -> y bf16 [N,H]."""
+    torch = _torch()
+    _need(act, "act", torch.uint8)
+    dev = act.device
+    N, I = act.shape
+    E, H, I2 = w2.shape
+    if I2 != I:
+        raise ValueError("w2 must be [E, H, I]")
+    _need(act_scales, "act_scales", torch.float32, (N, I // 128), dev)
+    _need(w2, "w2", torch.uint8, device=dev)
+    _need(w2_scales, "w2_scales", torch.float32, (E, H // 128, I // 128), dev)
+    _need(cnt_e, "cnt_e", torch.int32, (E,), dev)
+    if capacity == 0:
+        _need(off_e, "off_e", torch.int32, (E + 1,), dev)
+    if y is None:
+        y = torch.empty((N, H), dtype=torch.bfloat16, device=dev)
+    else:
+        _need(y, "y", torch.bfloat16, (N, H), dev)
+    cfg = MlpCfg(N, H, I, E, capacity)
+    _check(lib().moe_expert_down(ctypes.byref(cfg), _ptr(cnt_e), _ptr(off_e), _ptr(act), _ptr(act_scales),
+                                 _ptr(w2), _ptr(w2_scales), _ptr(y), _stream(dev)))
+    return y
 
 
 def combine(y, pos, topk_w, out=None, units_per_wave: int = 0):

@@ -19,7 +19,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libcgl_moe.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
-SOURCES = ["moe_api.hip", "route.hip", "layout.hip", "dispatch.hip", "combine.hip", "backward.hip", "fused.hip"]
+SOURCES = ["moe_api.hip", "route.hip", "layout.hip", "dispatch.hip", "combine.hip", "backward.hip", "fused.hip", "mlp.hip"]
 ARCH = os.environ.get("CGL_OFFLOAD_ARCH", "gfx950")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -68,7 +68,7 @@ using namespace cgl;
 
 extern "C" {
 
-int32_t moe_abi_version(void) { return 3; }
+int32_t moe_abi_version(void) { return 4; }
 
 const char* moe_last_error(void) { return g_err; }
 
@@ -314,6 +314,59 @@ moe_status moe_combine_backward(const moe_combine_cfg* c, const uint16_t* grad_o
     return hip_status(launch_combine_backward(grad_out, y, pos, topk_w, grad_y, grad_w, T, c->hidden, c->topk, N,
                                               c->units_per_wave, (hipStream_t)stream),
                       "combine_backward launch");
+}
+
+static moe_status check_mlp_cfg(const moe_mlp_cfg* c, const char* who) {
+    if (!c) return fail(MOE_ERR_INVALID, "%s: cfg is NULL", who);
+    const int N = c->num_rows, H = c->hidden, I = c->inter, E = c->num_experts, C = c->capacity;
+    if (N < 0) return fail(MOE_ERR_INVALID, "%s: num_rows %d < 0", who, N);
+    if (H < 128 || H % 128 || H > 65536) return fail(MOE_ERR_INVALID, "%s: hidden %d must be a multiple of 128 in [128, 65536]", who, H);
+    if (I < 128 || I % 128 || I > 8192) return fail(MOE_ERR_INVALID, "%s: inter %d must be a multiple of 128 in [128, 8192]", who, I);
+    if (E < 1 || E > 512) return fail(MOE_ERR_INVALID, "%s: num_experts %d outside [1, 512]", who, E);
+    if (C < 0) return fail(MOE_ERR_INVALID, "%s: capacity %d < 0", who, C);
+    if ((int64_t)N * H >= (1ll << 40)) return fail(MOE_ERR_INVALID, "%s: N*H too large", who);
+    return MOE_OK;
+}
+
+moe_status moe_expert_up(const moe_mlp_cfg* c, const int32_t* cnt_e, const int32_t* off_e, const uint8_t* x,
+                         const float* x_scales, const uint8_t* w1, const float* w1_scales, uint8_t* act,
+                         float* act_scales, void* stream) {
+    const moe_status st = check_mlp_cfg(c, "expert_up");
+    if (st != MOE_OK) return st;
+    if (c->hidden > 8192) return fail(MOE_ERR_INVALID, "expert_up: hidden %d above 8192", c->hidden);
+    if (c->num_rows == 0) return ok();
+    if (!cnt_e || (c->capacity == 0 && !off_e) || !x || !x_scales || !w1 || !w1_scales || !act || !act_scales)
+        return fail(MOE_ERR_INVALID, "expert_up: NULL array");
+    if (!aligned(x, 16) || !aligned(w1, 16) || !aligned(act, 16) || !aligned(x_scales, 4) ||
+        !aligned(w1_scales, 4) || !aligned(act_scales, 4) || !aligned(cnt_e, 4) || !aligned(off_e, 4))
+        return fail(MOE_ERR_INVALID, "expert_up: code arrays must be 16-byte aligned, the others 4-byte");
+    const hipError_t pe = prepare_expert_mlp(true, c->num_rows, c->hidden, c->num_experts);
+    if (pe != hipSuccess)
+        return fail(MOE_ERR_HIP, "expert_up: setting %zu bytes of LDS: %s",
+                    expert_mlp_lds_bytes(c->num_rows, c->hidden, c->num_experts), hipGetErrorString(pe));
+    return hip_status(launch_expert_up(cnt_e, off_e, x, x_scales, w1, w1_scales, act, act_scales, c->num_rows,
+                                       c->hidden, c->inter, c->num_experts, c->capacity, (hipStream_t)stream),
+                      "expert_up launch");
+}
+
+moe_status moe_expert_down(const moe_mlp_cfg* c, const int32_t* cnt_e, const int32_t* off_e, const uint8_t* act,
+                           const float* act_scales, const uint8_t* w2, const float* w2_scales, uint16_t* y,
+                           void* stream) {
+    const moe_status st = check_mlp_cfg(c, "expert_down");
+    if (st != MOE_OK) return st;
+    if (c->num_rows == 0) return ok();
+    if (!cnt_e || (c->capacity == 0 && !off_e) || !act || !act_scales || !w2 || !w2_scales || !y)
+        return fail(MOE_ERR_INVALID, "expert_down: NULL array");
+    if (!aligned(act, 16) || !aligned(w2, 16) || !aligned(y, 16) || !aligned(act_scales, 4) ||
+        !aligned(w2_scales, 4) || !aligned(cnt_e, 4) || !aligned(off_e, 4))
+        return fail(MOE_ERR_INVALID, "expert_down: code and output arrays must be 16-byte aligned, the others 4-byte");
+    const hipError_t pe = prepare_expert_mlp(false, c->num_rows, c->inter, c->num_experts);
+    if (pe != hipSuccess)
+        return fail(MOE_ERR_HIP, "expert_down: setting %zu bytes of LDS: %s",
+                    expert_mlp_lds_bytes(c->num_rows, c->inter, c->num_experts), hipGetErrorString(pe));
+    return hip_status(launch_expert_down(cnt_e, off_e, act, act_scales, w2, w2_scales, y, c->num_rows, c->hidden,
+                                         c->inter, c->num_experts, c->capacity, (hipStream_t)stream),
+                      "expert_down launch");
 }
 
 moe_status moe_quantize_e4m3(const float* in, uint8_t* out, int64_t n, void* stream) {

@@ -40,6 +40,16 @@ hipError_t launch_fused_decode(const float* logits, const uint16_t* x, int32_t* 
                                int G, int g, int k, int n, int score_fn, int renorm, int R, int C, int A, int N,
                                int H, int dtype, hipStream_t stream);
 
+// Expert MLP (grouped FP8 GEMMs with power-of-two block scales).
+size_t expert_mlp_lds_bytes(int N, int K, int E);
+hipError_t prepare_expert_mlp(bool up, int N, int K, int E);
+hipError_t launch_expert_up(const int32_t* cnt_e, const int32_t* off_e, const uint8_t* x, const float* xs,
+                            const uint8_t* w1, const float* w1s, uint8_t* act, float* act_s, int N, int H, int I,
+                            int E, int C, hipStream_t stream);
+hipError_t launch_expert_down(const int32_t* cnt_e, const int32_t* off_e, const uint8_t* act, const float* act_s,
+                              const uint8_t* w2, const float* w2s, uint16_t* y, int N, int H, int I, int E, int C,
+                              hipStream_t stream);
+
 hipError_t launch_quantize_e4m3(const float* in, uint8_t* out, int64_t n, hipStream_t stream);
 
 }  // namespace cgl

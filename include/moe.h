@@ -304,6 +304,61 @@ moe_status moe_route_dispatch(const moe_route_cfg* route, const moe_layout_cfg* 
                               void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ */
+/* Expert MLP on the receive buffer: the two linear layers of every routed   */
+/* expert, between moe_dispatch and moe_combine.                            */
+/*                                                                          */
+/* Follows the Mega MoE news page (the MoE layer runs dispatch, a first     */
+/* linear layer, SwiGLU, a second linear layer and combine) and the         */
+/* TileKernels news page, "functions" (SwiGLU fused with the FP8            */
+/* quantisation): moe_expert_up computes the first layer and applies SwiGLU */
+/* and the FP8 requantisation in its epilogue, so the 2I-wide               */
+/* pre-activation never reaches memory; moe_expert_down computes the second */
+/* layer into the bf16 rows moe_combine reads.                              */
+/*                                                                          */
+/* Expert e owns receive rows [s_e, s_e + n_e): capacity 0: s_e = off_e[e], */
+/* n_e = cnt_e[e]; capacity C > 0: s_e = e*C, n_e = min(cnt_e[e], C) (the   */
+/* arrays moe_get_layout writes).  Rows outside every range are not         */
+/* written.  A layout whose ranges leave [0, N) makes that expert skipped.  */
+/* All operands are OCP E4M3FN codes with POWER-OF-TWO fp32 block scales    */
+/* (only the exponent bits are used; a scale that is not a power of two    */
+/* gives wrong results): activations one scale per row and 128 columns, as  */
+/* moe_dispatch(MOE_DISPATCH_FP8_E4M3_POW2) writes them; weights one per    */
+/* 128x128 block.  Accumulation is fp32 on the matrix cores.                */
+/*                                                                          */
+/* moe_expert_up:                                                           */
+/*   h[p, n]   = sum_k x(p,k) * w1(e,n,k), n < 2I (rows 0..I-1 gate, I..2I-1 */
+/*               up), x(p,k) = code * x_scales[p, k/128], w1 likewise with  */
+/*               w1_scales[e, n/128, k/128];                                */
+/*   a[p, j]   = silu(h[p,j]) * h[p, I+j], silu(g) = g / (1 + exp(-g));      */
+/*   act, act_scales = FP8 with power-of-two scales per 128 columns of a, by */
+/*               the FP8_E4M3_POW2 recipe of moe_dispatch.                  */
+/*   x uint8 [N,H], x_scales fp32 [N,H/128], w1 uint8 [E,2I,H], w1_scales   */
+/*   fp32 [E,2I/128,H/128] in; act uint8 [N,I], act_scales fp32 [N,I/128]   */
+/*   out.                                                                   */
+/* moe_expert_down:                                                         */
+/*   y[p, n]   = bf16_rne( sum_k act(p,k) * w2(e,n,k) ), n < H.             */
+/*   act uint8 [N,I], act_scales fp32 [N,I/128], w2 uint8 [E,H,I],           */
+/*   w2_scales fp32 [E,H/128,I/128] in; y bf16 [N,H] out.                   */
+/* Limits: H and I multiples of 128, H <= 8192 for up, I <= 8192,           */
+/* 1 <= E <= 512.  Code arrays and y 16-byte aligned.                       */
+/* ------------------------------------------------------------------------ */
+typedef struct {
+    int32_t num_rows;     /* N: rows of the receive buffer */
+    int32_t hidden;       /* H */
+    int32_t inter;        /* I: expert intermediate width */
+    int32_t num_experts;  /* E */
+    int32_t capacity;     /* 0: ranges from off_e/cnt_e; C > 0: padded ranges */
+} moe_mlp_cfg;
+
+moe_status moe_expert_up(const moe_mlp_cfg* cfg, const int32_t* cnt_e, const int32_t* off_e,
+                         const uint8_t* x, const float* x_scales, const uint8_t* w1,
+                         const float* w1_scales, uint8_t* act, float* act_scales, void* stream);
+
+moe_status moe_expert_down(const moe_mlp_cfg* cfg, const int32_t* cnt_e, const int32_t* off_e,
+                           const uint8_t* act, const float* act_scales, const uint8_t* w2,
+                           const float* w2_scales, uint16_t* y, void* stream);
+
+/* ------------------------------------------------------------------------ */
 /* moe_quantize_e4m3 -- the element conversion moe_dispatch uses, exposed   */
 /* on its own: out[i] = E4M3FN nearest-even of in[i], magnitudes above 448  */
 /* saturate to 448, sign kept (codes for NaN inputs are unspecified).       */
