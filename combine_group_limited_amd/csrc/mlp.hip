@@ -259,8 +259,11 @@ __global__ __launch_bounds__(Tile<WM>::kThreads) void mlp_kernel(MlpArgs a) {
 
     if constexpr (UP) {
         // ---- SwiGLU, row amax over the tile's 128 act columns, FP8 codes -----
+        // row strides padded by 16 bytes so the four rows a wave writes at
+        // once (4 apart) fall in different LDS banks
+        constexpr int kTS = kActN + 16;
         uint32_t* amx = (uint32_t*)stage;   // [2][kBM] |act| maxima of each wave column
-        uint8_t* tile = stage + 4096;       // [kBM][128] codes
+        uint8_t* tile = stage + 4096;       // [kBM][kTS] codes
         float av[4][4][4];
         uint32_t rm[4][4];
 #pragma unroll
@@ -296,17 +299,21 @@ __global__ __launch_bounds__(Tile<WM>::kThreads) void mlp_kernel(MlpArgs a) {
                 const uint32_t q = pack_e4m3x4(av[r][0][i] * inv, av[r][1][i] * inv, av[r][2][i] * inv,
                                                av[r][3][i] * inv);
 #pragma unroll
-                for (int c = 0; c < 4; ++c) tile[row * kActN + 64 * wc + 16 * c + lr] = (uint8_t)(q >> (8 * c));
+                for (int c = 0; c < 4; ++c) tile[row * kTS + 64 * wc + 16 * c + lr] = (uint8_t)(q >> (8 * c));
                 if (wc == 0 && lr == 0 && row < nvalid) a.act_s[(size_t)(row0 + row) * SI + n0 / kBK] = scale;
             }
         __syncthreads();
         for (int i = tid; i < kBM * 8; i += kThreads) {
             const int r = i >> 3, c = i & 7;
             if (r < nvalid)
-                *(u32x4*)(a.act + (size_t)(row0 + r) * a.I + n0 + c * 16) = *(const u32x4*)(tile + r * kActN + c * 16);
+                *(u32x4*)(a.act + (size_t)(row0 + r) * a.I + n0 + c * 16) = *(const u32x4*)(tile + r * kTS + c * 16);
         }
     } else {
-        // ---- BF16 output tile [kBM][256], staged for 16-byte stores ----------
+        // ---- BF16 output tile [kBM][256 + 8], staged for 16-byte stores ------
+        // (rows padded by 16 bytes: the four rows a wave writes at once fall
+        // in different LDS banks; the tile may run into the scale area, which
+        // is no longer needed)
+        constexpr int kTS = kBR + 8;
         uint16_t* tile = (uint16_t*)stage;
 #pragma unroll
         for (int r = 0; r < 4; ++r)
@@ -316,24 +323,29 @@ __global__ __launch_bounds__(Tile<WM>::kThreads) void mlp_kernel(MlpArgs a) {
                 for (int i = 0; i < 4; ++i) {
                     const int row = 64 * wr + 16 * r + 4 * g + i, col = 128 * wc + 16 * c + lr;
                     const __bf16 b = (__bf16)acc[r][c][i];
-                    tile[row * kBR + col] = __builtin_bit_cast(uint16_t, b);
+                    tile[row * kTS + col] = __builtin_bit_cast(uint16_t, b);
                 }
         __syncthreads();
         for (int i = tid; i < kBM * 32; i += kThreads) {
             const int r = i >> 5, c = i & 31;
             const int col = n0 + c * 8;
             if (r < nvalid && col < a.WR)
-                *(u32x4*)(a.y + (size_t)(row0 + r) * a.WR + col) = *(const u32x4*)(tile + r * kBR + c * 8);
+                *(u32x4*)(a.y + (size_t)(row0 + r) * a.WR + col) = *(const u32x4*)(tile + r * kTS + c * 8);
         }
     }
 }
 
+// Dynamic LDS: the stages, the scales and the tile prefix; at least the
+// epilogue's staging tile, which reuses the same bytes from the start.
 template <int WM>
 size_t lds_bytes_for(int K, int E) {
     using TL = Tile<WM>;
     const int KB = K / kBK;
-    return TL::kStages * (size_t)TL::kStageBytes + (((size_t)TL::kBM * KB + 2 * KB + 15) & ~(size_t)15) +
-           4 * (2 * (size_t)E + 1);
+    const size_t loop = TL::kStages * (size_t)TL::kStageBytes + (((size_t)TL::kBM * KB + 2 * KB + 15) & ~(size_t)15) +
+                        4 * (2 * (size_t)E + 1);
+    const size_t up_tile = 4096 + (size_t)TL::kBM * (kActN + 16);
+    const size_t down_tile = (size_t)TL::kBM * (kBR + 8) * 2;
+    return loop > up_tile ? (loop > down_tile ? loop : down_tile) : (up_tile > down_tile ? up_tile : down_tile);
 }
 
 // 256-row tiles when experts average at least 512 rows, else 128-row tiles.
