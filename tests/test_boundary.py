@@ -177,3 +177,34 @@ def test_route_dispatch_workspace_size():
 def test_route_dispatch_rejects(rc, lc, dc, status):
     assert _route_dispatch(rc, lc, dc) == status
     assert moe.lib().moe_last_error()
+
+
+def _mlp(fn, cfg_vals, n_args):
+    L = moe.lib()
+    cfg = moe.MlpCfg(*cfg_vals)
+    return getattr(L, fn)(ctypes.byref(cfg), *([None] * n_args))
+
+
+@pytest.mark.parametrize("fn,n_args", [("moe_expert_up", 9), ("moe_expert_down", 8)])
+@pytest.mark.parametrize("vals", [
+    (100, 7000, 2048, 8, 0),      # hidden not a multiple of 128
+    (100, 7168, 2000, 8, 0),      # inter not a multiple of 128
+    (100, 7168, 2048, 0, 0),      # no experts
+    (100, 7168, 2048, 513, 0),    # too many experts
+    (100, 7168, 2048, 8, -1),     # negative capacity
+    (-1, 7168, 2048, 8, 0),       # negative rows
+    (100, 7168, 16384, 8, 0),     # inter above 8192
+    (100, 7168, 2048, 8, 0),      # valid shape, NULL arrays
+])
+def test_expert_mlp_rejects(fn, n_args, vals):
+    assert _mlp(fn, vals, n_args) == moe.MOE_ERR_INVALID
+    assert moe.lib().moe_last_error()
+
+
+def test_expert_up_rejects_hidden_above_8192():
+    assert _mlp("moe_expert_up", (100, 16384, 2048, 8, 0), 9) == moe.MOE_ERR_INVALID
+
+
+@pytest.mark.parametrize("fn,n_args", [("moe_expert_up", 9), ("moe_expert_down", 8)])
+def test_expert_mlp_zero_rows_is_noop(fn, n_args):
+    assert _mlp(fn, (0, 7168, 2048, 8, 0), n_args) == moe.MOE_OK
