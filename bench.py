@@ -394,7 +394,7 @@ def main():
     evs_cold = [hev.create(5) for _ in range(K)]
     torch.cuda.synchronize()
     for i in range(K):
-        torch.sum(flush, out=flush_sum)
+        torch.sum(flush, dim=0, out=flush_sum)
         step(i, evs_cold[i])
     torch.cuda.synchronize()
     del flush

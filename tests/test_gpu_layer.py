@@ -71,7 +71,8 @@ def test_layer_stages_fit_together(T, H, I, E, G, g, k, R, A):
     assert np.all(off[:-1] % A == 0)
     d = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
     act, act_s = moe.expert_up(rx, rs, d(w1), d(w1s), lay.cnt_e, lay.off_e)
-    y = moe.expert_down(act, act_s, d(w2), d(w2s), lay.cnt_e, lay.off_e)
+    y = moe.expert_down(act, act_s, d(w2), d(w2s), lay.cnt_e, lay.off_e,
+                        y=torch.zeros((N, H), dtype=torch.bfloat16, device=DEV))
     act_g, act_s_g = act.cpu().numpy(), act_s.cpu().numpy()
     # up against the oracle on sampled rows of every non-empty expert
     rows = np.array(sorted({int(off[e] + j) for e in range(E) if cnt[e] > 0
