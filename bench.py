@@ -505,6 +505,29 @@ def main():
                 "ms_per_step_without_stage_events": round(hev.ms(fs, fe) / K, 4),
                 "separate_route_layout_dispatch_us": round(route_us + layout_us + disp_us, 2),
             }
+            # both decode steps captured in a HIP graph and replayed K times
+            # (inputs of set 0; the graph holds only this library's kernels)
+            for name, fn in (("graph_step_us_separate", lambda: step(0)), ("graph_step_us_one_launch",
+                                                                           lambda: fstep(0))):
+                side = torch.cuda.Stream()
+                side.wait_stream(torch.cuda.current_stream())
+                with torch.cuda.stream(side):
+                    fn()
+                torch.cuda.current_stream().wait_stream(side)
+                torch.cuda.synchronize()
+                graph = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(graph):
+                    fn()
+                graph.replay()
+                torch.cuda.synchronize()
+                gs, ge = hev.create(2)
+                hev.record(gs, stream)
+                for _ in range(K):
+                    graph.replay()
+                hev.record(ge, stream)
+                torch.cuda.synchronize()
+                res["one_launch_decode"][name] = round(hev.ms(gs, ge) / K * 1e3, 2)
+                del graph
         except moe.MoeError as e:
             res["one_launch_decode"] = {"unsupported": str(e)}
 
