@@ -112,16 +112,17 @@ def source_digest(*names):
     return h.hexdigest()[:16]
 
 
-def load_traffic(kernel: str, digest: str):
+def load_traffic(kernel: str, digest: str, workload: str):
     """HBM bytes per launch measured with rocprofv3 counters (profiles/traffic.json),
-    only while the kernel's sources are unchanged since the measurement."""
+    only for the workload they were taken on and while the kernel's sources are
+    unchanged since the measurement."""
     p = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(p):
         return None
     with open(p) as f:
         data = json.load(f)
     ent = data.get(kernel)
-    if not ent or ent.get("source_digest") != digest:
+    if not ent or ent.get("source_digest") != digest or ent.get("workload") != workload:
         return None
     return ent.get("bytes_per_launch")
 
@@ -287,7 +288,7 @@ def mlp_main(args, torch, moe, hev, dev):
         "roofline": {"kernel": f"mlp_kernel<{'true' if dom == 'up' else 'false'}> ({dom})", "bound": "mfma",
                      "achieved": round(ach, 1), "peak": FP8_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(ach / FP8_MFMA_PEAK_TFLOPS, 4),
-                     "traffic": load_traffic("mlp_" + dom, digest),
+                     "traffic": load_traffic("mlp_" + dom, digest, wl.name),
                      "algorithmic_flops": f_up if dom == "up" else f_down,
                      "avg_launch_us": round(up_us if dom == "up" else down_us, 1), "source_digest": digest},
     }
@@ -418,7 +419,7 @@ def main():
     digest = source_digest(*dom_src)
     roof = {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
             "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": load_traffic(dom, digest), "algorithmic_bytes": dom_bytes,
+            "traffic": load_traffic(dom, digest, wl.name), "algorithmic_bytes": dom_bytes,
             "avg_launch_us": round(dom_us, 2), "source_digest": digest}
 
     res = {
