@@ -10,27 +10,33 @@
 //
 // Operands are OCP E4M3FN with power-of-two block scales -- activations one
 // per row and 128 columns (as dispatch's FP8_E4M3_POW2 writes them), weights
-// one per 128x128 block -- so each 128-deep step is one
-// v_mfma_scale_f32_16x16x128_f8f6f4 per 16x16 output tile with both scales
+// one per 128x128 block -- so each 64-deep step is one
+// v_mfma_scale_f32_32x32x64_f8f6f4 per 32x32 output tile with both scales
 // handed to the instruction as E8M0 exponents: no rescaling on the vector
-// units.  Operand lane layout of the instruction (measured): lane l holds
-// row l%16 and K bytes [16g, 16g+16) and [64+16g, 64+16g+16), g = l/16; the
-// E8M0 scale of (row m, 32-deep K block q) is taken from lane 16q+m, so with
-// 128-deep scale blocks every lane passes its own row's scale; accumulator
-// element i of lane l is row 4g+i, column l%16.
+// units.  Instruction facts used (measured on gfx950): lane l supplies row
+// l%32 of each operand and one half of the 64-deep K range (which bytes does
+// not matter as long as both operands agree, since a 128-deep scale block
+// covers the whole step); lane l also supplies the scale of row l%32, and the
+// op_sel field picks which byte of the 32-bit scale register is used, so the
+// scales of four row tiles travel in one register; accumulator element i of
+// lane l is row 8(i/4) + 4(l/32) + i%4, column l%32.
 //
-// Tiles: a block of 2*WM waves owns BM = 64*WM rows of one expert x 256
-// weight rows (up: 128 gate rows and the matching 128 up rows; down: 256
-// output columns); wave (wr, wc) owns 64 rows x 128 weight rows = 4 x 8 MFMA
-// tiles.  WM = 4 (256 rows, 8 waves, two waves per SIMD) for experts with
-// many rows; WM = 2 (128 rows, 4 waves) otherwise.  The K loop stages
-// 128-deep slices of both operands in LDS (three stages of 48 KiB for WM = 2,
-// two of 64 KiB for WM = 4), filled by direct global->LDS copies issued one
-// or two slices ahead; 16-byte chunks are XOR-swizzled by row so fragment
-// reads are conflict-free.  Expert row ranges come from the layout (off_e and
-// cnt_e, or e*C and min(cnt_e, C) when padded); each block finds its
-// (expert, row tile) from the per-expert tile counts, so the grid is sized
-// without reading anything back to the host.
+// Tiles: a block of four waves (2 x 2) owns BM = 64*TM rows of one expert x
+// 256 weight rows; wave (wr, wc) owns 32*TM rows x 128 weight rows = TM x 4
+// MFMA tiles (TM = 4: 256 accumulators per lane, one wave per SIMD).  Up:
+// the block's weight rows are 128 gate rows and the matching 128 up rows, and
+// wave wc takes gate rows 64wc.. and the same up rows, so SwiGLU pairs
+// registers of one lane; down: 256 output columns.  The K loop stages
+// 128-deep slices of both operands (whole 128-byte lines per row) in two LDS
+// buffers filled by direct global->LDS copies; 16-byte chunks are
+// XOR-swizzled by row so fragment reads are conflict-free.  Each stage is
+// computed as two 64-deep halves with two register sets, so the fragments of
+// the next half are read while the MFMAs of the current one run, and one
+// barrier per stage publishes the next stage and frees a buffer for the one
+// after.  Expert row ranges come from the layout (off_e and cnt_e, or e*C and
+// min(cnt_e, C) when padded); each block finds its (expert, row tile) from
+// the per-expert tile counts, so the grid is sized without reading anything
+// back to the host.
 #include "moe_device.hpp"
 #include "moe_internal.hpp"
 
@@ -40,28 +46,27 @@ namespace {
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int kBK = 128;    // K per step (one scale block)
+constexpr int kBK = 128;    // K per scale block = K per LDS stage
 constexpr int kBR = 256;    // weight rows per block tile
 constexpr int kActN = 128;  // up: act columns per block (128 gate + 128 up weight rows)
+constexpr int kThreads = 256;
 
-// s_waitcnt vmcnt(N) with expcnt and lgkmcnt at their "no wait" maxima
-template <int N>
+// s_waitcnt vmcnt(N) (6-bit count split over bits 3:0 and 15:14), with
+// expcnt at its "no wait" maximum and lgkmcnt either at its maximum (LGKM =
+// false) or 0
+template <int N, bool LGKM = false>
 __device__ __forceinline__ void wait_vm() {
-    static_assert(N >= 0 && N < 16, "vmcnt field");
-    __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+    static_assert(N >= 0 && N < 64, "vmcnt field");
+    __builtin_amdgcn_s_waitcnt((LGKM ? 0x0070 : 0x0F70) | (N & 15) | ((N >> 4) << 14));
 }
 
-template <int WM>
+template <int TM>
 struct Tile {
-    static constexpr int kWaves = 2 * WM;
-    static constexpr int kThreads = 64 * kWaves;
-    static constexpr int kBM = 64 * WM;                    // rows per block
-    static constexpr int kStageBytes = (kBM + kBR) * kBK;  // A slice, then B slice
-    static constexpr int kStages = WM == 2 ? 3 : 2;
-    static constexpr int kCopiesA = kBM / 8 / kWaves;      // 1 KiB copies per wave per slice
-    static constexpr int kCopiesB = kBR / 8 / kWaves;
-    static constexpr int kCopies = kCopiesA + kCopiesB;
+    static constexpr int kBM = 64 * TM;                    // rows per block
+    static constexpr int kStageBytes = (kBM + kBR) * kBK;  // A stage, then B stage
+    static constexpr int kCopies = (kBM + kBR) / 8 / 4;    // 1 KiB copies per wave per stage
 };
 
 struct MlpArgs {
@@ -77,7 +82,7 @@ struct MlpArgs {
     int N, K, WR, E, C, I;
 };
 
-__device__ __forceinline__ int e8m0(float s) { return (int)((__float_as_uint(s) >> 23) & 0xFFu); }
+__device__ __forceinline__ uint32_t e8m0(float s) { return (__float_as_uint(s) >> 23) & 0xFFu; }
 
 __device__ __forceinline__ int rows_of(const MlpArgs& a, int e, int& start) {
     int cnt = a.cnt_e[e];
@@ -92,9 +97,15 @@ __device__ __forceinline__ int rows_of(const MlpArgs& a, int e, int& start) {
     return cnt;
 }
 
-// LDS offset of 16-byte chunk c of row r in a 128-byte-row slice.
-__device__ __forceinline__ int swz(int r, int c) { return r * kBK + ((c ^ (r & 7)) << 4); }
+// XOR swizzle of the 16-byte chunks of a 128-byte-row stage.  A 16-byte LDS
+// read is served 16 lanes at a time from 64 four-byte banks (256 bytes); 16
+// lanes read 16 consecutive rows at one logical chunk, rows of equal parity
+// share a 128-byte bank half, and the key (r >> 1) & 7 gives the eight rows
+// of each parity distinct chunks, so the 16 reads hit distinct banks.
+__device__ __forceinline__ int swz_key(int r) { return (r >> 1) & 7; }
+__device__ __forceinline__ int swz(int r, int c) { return r * kBK + ((c ^ swz_key(r)) << 4); }
 
+// Weight row (within the expert's [WR, K] matrix) staged at B-slice row r.
 template <bool UP>
 __device__ __forceinline__ int wrow_of(const MlpArgs& a, int n0, int r) {
     if constexpr (UP) return r < kActN ? n0 + r : a.I + n0 + (r - kActN);
@@ -108,20 +119,49 @@ __device__ __forceinline__ void bare_barrier() {
     asm volatile("" ::: "memory");
 }
 
-template <bool UP, int WM>
-__global__ __launch_bounds__(Tile<WM>::kThreads) void mlp_kernel(MlpArgs a) {
-    using TL = Tile<WM>;
-    constexpr int kThreads = TL::kThreads, kBM = TL::kBM, kStageBytes = TL::kStageBytes, kStages = TL::kStages;
+// Max of non-negative 32-bit values over each half-wave (lanes 0-31, 32-63).
+__device__ __forceinline__ uint32_t half32_max_u32(uint32_t v) {
+    v = row16_max_u32(v);
+    return max(v, (uint32_t)__shfl_xor((int)v, 16, 64));
+}
+
+// One scaled 32x32x64 MFMA; OA and OB pick the scale bytes.
+template <int OA, int OB>
+__device__ __forceinline__ f32x16 mfma32(const i32x8& a, const i32x8& b, const f32x16& c, uint32_t sa, uint32_t sb) {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, OA, (int)sa, OB, (int)sb);
+}
+
+template <int TM>
+struct Frag {
+    i32x8 a[TM];
+    i32x8 b[4];
+    uint32_t sa, sb;
+};
+
+template <bool UP, int TM, int T, int U>
+__device__ __forceinline__ void mma_tile(f32x16 (&acc)[TM][4], const Frag<TM>& f) {
+    // op_sel picks byte T of the A scales and, for up, byte 0 (gate) or 1
+    // (up) of the weight scales
+    acc[T][U] = mfma32<T, (UP && U >= 2) ? 1 : 0>(f.a[T], f.b[U], acc[T][U], f.sa, f.sb);
+    if constexpr (U + 1 < 4) mma_tile<UP, TM, T, U + 1>(acc, f);
+    else if constexpr (T + 1 < TM) mma_tile<UP, TM, T + 1, 0>(acc, f);
+}
+
+template <bool UP, int TM>
+__global__ __launch_bounds__(kThreads) void mlp_kernel(MlpArgs a) {
+    using TL = Tile<TM>;
+    constexpr int kBM = TL::kBM, kStageBytes = TL::kStageBytes, kCopies = TL::kCopies;
     extern __shared__ __align__(16) uint8_t smem[];
-    uint8_t* stage = smem;                                  // [kStages][kStageBytes]
+    uint8_t* ring = smem;                                          // [2][kStageBytes]
     const int KB = a.K / kBK;
-    uint8_t* a_sc = smem + kStages * kStageBytes;           // [kBM][KB] E8M0
-    uint8_t* w_sc = a_sc + kBM * KB;                        // [2][KB]
-    int32_t* tot = (int32_t*)(smem + kStages * kStageBytes + ((kBM * KB + 2 * KB + 15) & ~15));
-    int32_t* tpref = tot + a.E;                             // [E+1]
+    uint32_t* a_sc = (uint32_t*)(smem + 2 * kStageBytes);          // [KB][2][32]: byte t = row tile t
+    uint32_t* w_sc = a_sc + KB * 64;                               // [KB][2]
+    int32_t* tot = (int32_t*)(w_sc + 2 * KB);                      // [E]
+    int32_t* tpref = tot + a.E;                                    // [E+1]
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, w = tid >> 6, wr = w >> 1, wc = w & 1, g = lane >> 4, lr = lane & 15;
+    const int lane = tid & 63, w = tid >> 6, wr = w >> 1, wc = w & 1;
+    const int m = lane & 31, g = lane >> 5;
 
     // ---- which expert and row tile this block computes --------------------
     for (int e = tid; e < a.E; e += kThreads) {
@@ -144,185 +184,239 @@ __global__ __launch_bounds__(Tile<WM>::kThreads) void mlp_kernel(MlpArgs a) {
     const int nvalid = min(kBM, start + cnt - row0);
     const int n0 = blockIdx.x * (UP ? kActN : kBR);
 
+    // ---- K loop -----------------------------------------------------------
+    // One 128-deep stage (kBM rows of A and 256 weight rows, 128 bytes each)
+    // goes to LDS by direct global->LDS copies: each instruction moves 1 KiB
+    // (8 rows) with lane i filling LDS bytes [16i, 16i+16), so lane i fetches
+    // the logical chunk that the swizzle puts at that position.  Each copy's
+    // rows are all A rows or all weight rows, so it takes a wave-uniform base
+    // and a 32-bit row offset.  Whole 128-byte lines per row matter: the same
+    // traffic in 64-byte halves moves 25 % slower into the CUs.
+    const uint8_t* wbase = a.w + (size_t)e * a.WR * a.K;
+    const int wv = wave_in_block();  // w, as a scalar
+    const int rl = lane >> 3;        // row within the 8-row group
+    uint32_t coff[kCopies];
+#pragma unroll
+    for (int j = 0; j < kCopies; ++j) {
+        const int q = wv * kCopies + j, r = 8 * q + rl;
+        const int row = r < kBM ? min(row0 + r, a.N - 1) : wrow_of<UP>(a, n0, r - kBM);
+        const int lc = (lane & 7) ^ swz_key(r);  // logical chunk held at this lane's position
+        coff[j] = (uint32_t)row * (uint32_t)a.K + (uint32_t)(lc * 16);
+    }
+    // Stages past the end are replaced by copies of one line that nobody
+    // reads, so the loop needs no branch around its copies.
+    auto issue = [&](int st, int buf) {
+        uint8_t* d = ring + buf * kStageBytes;
+        const bool real = st < KB;
+        const uint32_t kof = real ? (uint32_t)(st * kBK) : 0u;
+#pragma unroll
+        for (int j = 0; j < kCopies; ++j) {
+            const int q = wv * kCopies + j;
+            const uint8_t* base = 8 * q < kBM ? a.a : wbase;
+            const uint32_t off = real ? coff[j] + kof : 0u;
+            __builtin_amdgcn_global_load_lds((const void*)(base + off),
+                                             (__attribute__((address_space(3))) void*)(d + q * 1024), 16, 0, 0);
+        }
+    };
+
+    // Fragments of one 64-deep half of a stage: TM row tiles of A and 4
+    // weight tiles, 32 bytes per lane each (chunks 4h + 2g and 4h + 2g + 1 of
+    // the lane's row), and the stage's scales.
+    const int arow0 = 32 * TM * wr + m;
+    int brow[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        if constexpr (UP) brow[u] = (u < 2 ? 0 : kActN) + 64 * wc + 32 * (u & 1) + m;
+        else brow[u] = 128 * wc + 32 * u + m;
+    }
+    auto read = [&](Frag<TM>& f, int st, int buf, int h) {
+        const uint8_t* sA = ring + buf * kStageBytes;
+        const uint8_t* sB = sA + kBM * kBK;
+        const int c0 = 4 * h + 2 * g;
+#pragma unroll
+        for (int t = 0; t < TM; ++t) {
+            const int row = arow0 + 32 * t;
+            const i32x4 lo4 = *(const i32x4*)(sA + swz(row, c0));
+            const i32x4 hi4 = *(const i32x4*)(sA + swz(row, c0 + 1));
+            f.a[t] = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const i32x4 lo4 = *(const i32x4*)(sB + swz(brow[u], c0));
+            const i32x4 hi4 = *(const i32x4*)(sB + swz(brow[u], c0 + 1));
+            f.b[u] = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
+        }
+        f.sa = a_sc[(st * 2 + wr) * 32 + m];
+        f.sb = w_sc[st * 2 + wc];
+    };
+
+    f32x16 acc[TM][4];
+#pragma unroll
+    for (int t = 0; t < TM; ++t)
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[t][u][i] = 0.0f;
+
+    // Stage protocol (two buffers; stage S lives in buffer S % 2).  Each
+    // stage is two MFMA halves.  During half 0 of S the wave reads the
+    // fragments of half 1 of S; then every wave waits until its copies of
+    // stage S+1 have landed (they are the only ones outstanding) and its own
+    // reads are done, and meets the others at a bare barrier: S+1 is now
+    // visible to all and buffer S % 2 is free, so stage S+2 is issued into
+    // it, and half 1 of S runs while half 0 of S+1 is read.  One barrier per
+    // stage; a stage's copies have a whole stage of MFMAs to land.
+    Frag<TM> f0, f1;
+    issue(0, 0);
+    issue(1, 1);
     // ---- scales of the whole K range, as E8M0 bytes ------------------------
-    for (int i = tid; i < kBM * KB; i += kThreads) {
-        const int r = i / KB, kb = i - r * KB;
-        const int row = min(row0 + r, a.N - 1);
-        a_sc[i] = (uint8_t)e8m0(a.as[(size_t)row * KB + kb]);
+    // Issued after the first slices' copies so both latencies overlap.  a_sc
+    // word (kb, wr, m) holds the scales of rows 32*TM*wr + 32t + m (t < TM)
+    // in byte t (bytes >= TM are never read).
+    {
+        // the block's kBM x KB scales are one contiguous run of a.as (reads
+        // past the array's end take its last element: those rows are never
+        // stored): thread i takes elements i, i + 256, ..., sixteen loads in
+        // flight at a time; (row, kb) of each element is stepped, not divided
+        const int n = kBM * KB;
+        const float* src = a.as + (size_t)row0 * KB;
+        const int last = min(n, (a.N - row0) * KB) - 1;
+        const int dq = kThreads / KB, dr = kThreads - dq * KB;
+        int r = tid / KB, kb = tid - r * KB;
+        for (int j0 = 0; j0 * kThreads < n; j0 += 16) {
+            float v[16];
+#pragma unroll
+            for (int j = 0; j < 16; ++j) v[j] = src[min(tid + (j0 + j) * kThreads, last)];
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                if (tid + (j0 + j) * kThreads < n)
+                    ((uint8_t*)a_sc)[kb * 256 + ((r / (32 * TM)) * 32 + (r & 31)) * 4 + (r / 32) % TM] =
+                        (uint8_t)e8m0(v[j]);
+                r += dq;
+                kb += dr;
+                if (kb >= KB) {
+                    kb -= KB;
+                    ++r;
+                }
+            }
+        }
     }
     const int WRB = a.WR / kBK;
     for (int i = tid; i < 2 * KB; i += kThreads) {
-        const int which = i / KB, kb = i - which * KB;
-        int blk;
-        if constexpr (UP) blk = (which == 0 ? n0 : a.I + n0) / kBK;
-        else blk = min(n0 / kBK + which, WRB - 1);
-        w_sc[i] = (uint8_t)e8m0(a.ws[((size_t)e * WRB + blk) * KB + kb]);
+        const int kb = i >> 1, which = i & 1;
+        uint32_t v;
+        if constexpr (UP) {  // byte 0 the gate block, byte 1 the up block (both wave columns)
+            const size_t base = (size_t)e * WRB * KB + kb;
+            v = e8m0(a.ws[base + (size_t)(n0 / kBK) * KB]) | (e8m0(a.ws[base + (size_t)((a.I + n0) / kBK) * KB]) << 8);
+        } else {             // the wave column's 128 output rows
+            const int blk = min(n0 / kBK + which, WRB - 1);
+            v = e8m0(a.ws[((size_t)e * WRB + blk) * KB + kb]);
+        }
+        w_sc[i] = v;
     }
-
-    // ---- K loop -----------------------------------------------------------
-    const uint8_t* wbase = a.w + (size_t)e * a.WR * a.K;
-    // One slice (kBM rows of A and 256 weight rows, 128 bytes each) goes to
-    // LDS by direct global->LDS copies: each instruction moves 1 KiB (8 rows)
-    // with lane i filling LDS bytes [16i, 16i+16), so lane i fetches the
-    // logical chunk that the swizzle puts at that position.
-    const int pc = lane & 7, rl = lane >> 3;  // physical chunk, row within the 8-row group
-    const int lc = pc ^ rl;                   // logical chunk held there
-    auto issue = [&](int kb, int st) {
-        uint8_t* sA = stage + st * kStageBytes;
-#pragma unroll
-        for (int j = 0; j < TL::kCopiesA; ++j) {
-            const int q = TL::kCopiesA * w + j, r = 8 * q + rl;
-            const int row = min(row0 + r, a.N - 1);
-            __builtin_amdgcn_global_load_lds((const void*)(a.a + (size_t)row * a.K + kb * kBK + lc * 16),
-                                             (__attribute__((address_space(3))) void*)(sA + q * 1024), 16, 0, 0);
-        }
-#pragma unroll
-        for (int j = 0; j < TL::kCopiesB; ++j) {
-            const int q = TL::kCopiesB * w + j, r = 8 * q + rl;
-            __builtin_amdgcn_global_load_lds(
-                (const void*)(wbase + (size_t)wrow_of<UP>(a, n0, r) * a.K + kb * kBK + lc * 16),
-                (__attribute__((address_space(3))) void*)(sA + kBM * kBK + q * 1024), 16, 0, 0);
-        }
-    };
-
-    f32x4 acc[4][8];
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-#pragma unroll
-        for (int c = 0; c < 8; ++c) acc[r][c] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-
-    // 32 MFMAs of one 128-deep slice from LDS stage st
-    auto compute = [&](int kb, int st) {
-        const uint8_t* sA = stage + st * kStageBytes;
-        const uint8_t* sB = sA + kBM * kBK;
-        i32x8 af[4];
-        int sa[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int row = 64 * wr + 16 * r + lr;
-            const i32x4 lo4 = *(const i32x4*)(sA + swz(row, g));
-            const i32x4 hi4 = *(const i32x4*)(sA + swz(row, g + 4));
-            af[r] = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
-            sa[r] = a_sc[row * KB + kb];
-        }
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-            int brow, sb;
-            if constexpr (UP) {
-                brow = (c < 4) ? 64 * wc + 16 * c : kActN + 64 * wc + 16 * (c - 4);
-                sb = w_sc[(c < 4 ? 0 : 1) * KB + kb];
-            } else {
-                brow = 128 * wc + 16 * c;
-                sb = w_sc[wc * KB + kb];
-            }
-            const int row = brow + lr;
-            const i32x4 lo4 = *(const i32x4*)(sB + swz(row, g));
-            const i32x4 hi4 = *(const i32x4*)(sB + swz(row, g + 4));
-            const i32x8 bf = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                acc[r][c] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[r], bf, acc[r][c], 0, 0, 0, sa[r],
-                                                                             0, sb);
-        }
-    };
-
-    // kStages-1 slices are in flight while one is multiplied.  Before each
-    // barrier every wave waits until only its copies of the newer slices are
-    // outstanding (s_waitcnt vmcnt counts them in issue order), so the barrier
-    // publishes the next slice.  The barrier is the bare instruction: a
-    // __syncthreads() release would also wait for the newest slice.  The
-    // steady-state loop is unconditional so that nothing moves across its
-    // wait; sched_barrier keeps the wait behind the slice's MFMAs.
-    constexpr int kAhead = kStages - 1;
-    constexpr int kLeft = (kAhead - 1) * TL::kCopies;  // copies allowed in flight at the barrier
     __syncthreads();  // scales in LDS
-    for (int s = 0; s < kAhead; ++s)
-        if (s < KB) issue(s, s);
-    if (KB >= kAhead) wait_vm<kLeft>();
-    else wait_vm<0>();
+    wait_vm<0>();     // both stages too (the scale loads were issued after them)
     bare_barrier();
-    int kb = 0;
-    for (; kb + kAhead < KB; ++kb) {
-        issue(kb + kAhead, (kb + kAhead) % kStages);
-        compute(kb, kb % kStages);
+    read(f0, 0, 0, 0);
+
+    constexpr int kM = 4 * TM;
+    constexpr int kDs = (2 * (TM + 4) + 2 + kM - 1) / kM;  // LDS reads per MFMA slot
+    constexpr int kVm = (kCopies + kM - 1) / kM;           // copies per MFMA slot
+    int st = 0;
+    for (; st + 1 < KB; ++st) {
+        const int b = st & 1;
+        read(f1, st, b, 1);
+        mma_tile<UP, TM, 0, 0>(acc, f0);
+#pragma unroll
+        for (int i = 0; i < kM; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, kDs, 0);  // LDS reads
+        }
         __builtin_amdgcn_sched_barrier(0);
-        wait_vm<kLeft>();
+        wait_vm<0, true>();
         bare_barrier();
-    }
-    for (; kb < KB; ++kb) {  // the last slices: nothing more to issue
-        compute(kb, kb % kStages);
+        issue(st + 2, b);
+        read(f0, st + 1, b ^ 1, 0);
+        mma_tile<UP, TM, 0, 0>(acc, f1);
+#pragma unroll
+        for (int i = 0; i < kM; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x020, kVm, 0);  // global->LDS copies
+            __builtin_amdgcn_sched_group_barrier(0x100, kDs, 0);  // LDS reads
+        }
         __builtin_amdgcn_sched_barrier(0);
-        wait_vm<0>();
-        bare_barrier();
     }
-    __syncthreads();
+    // the last stage
+    read(f1, st, st & 1, 1);
+    mma_tile<UP, TM, 0, 0>(acc, f0);
+    wait_vm<0, true>();
+    mma_tile<UP, TM, 0, 0>(acc, f1);
+    __syncthreads();  // every copy has landed (waited above); the ring is reused below
+
 
     if constexpr (UP) {
-        // ---- SwiGLU, row amax over the tile's 128 act columns, FP8 codes -----
-        // row strides padded by 16 bytes so the four rows a wave writes at
-        // once (4 apart) fall in different LDS banks
-        constexpr int kTS = kActN + 16;
-        uint32_t* amx = (uint32_t*)stage;   // [2][kBM] |act| maxima of each wave column
-        uint8_t* tile = stage + 4096;       // [kBM][kTS] codes
-        float av[4][4][4];
-        uint32_t rm[4][4];
+        // ---- SwiGLU into an fp32 LDS tile, then one thread per row: row amax
+        // over the block's 128 act columns, power-of-two scale, FP8 codes ----
+        // The lane holds, for row tile t and element i, row 32*TM*wr + 32t +
+        // 8(i/4) + 4g + i%4 at act column 64wc + 32u + m (u = 0, 1), so four
+        // consecutive elements are four consecutive rows of one column: the
+        // tile is column-major with columns padded to kBM + 4 floats (16-byte
+        // stores, lanes of a row group on distinct banks).  SwiGLU uses the
+        // hardware exp2 and reciprocal (1 ulp each; relative error below
+        // |g|*2^-24 + 2^-21 for the gate value g).
+        constexpr int kCS = kBM + 4;
+        float* ft = (float*)ring;  // [128][kCS]
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
+        for (int t = 0; t < TM; ++t)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                uint32_t m = 0;
+            for (int u = 0; u < 2; ++u)
 #pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    const float gg = acc[r][c][i], uu = acc[r][c + 4][i];
-                    const float v = gg / (1.0f + exp_fixed(-gg)) * uu;
-                    av[r][c][i] = v;
-                    m = max(m, __float_as_uint(v) & 0x7FFFFFFFu);
+                for (int k = 0; k < 4; ++k) {
+                    f32x4 v;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const float gg = acc[t][u][4 * k + j], uu = acc[t][u + 2][4 * k + j];
+                        v[j] = gg * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(gg * -1.44269504f)) * uu;
+                    }
+                    const int row = 32 * TM * wr + 32 * t + 8 * k + 4 * g, col = 64 * wc + 32 * u + m;
+                    *(f32x4*)(ft + col * kCS + row) = v;
                 }
-                rm[r][i] = row16_max_u32(m);
-            }
-        if (lr == 0)
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) amx[wc * kBM + 64 * wr + 16 * r + 4 * g + i] = rm[r][i];
         __syncthreads();
-        const int SI = a.I / kBK;
+        if (tid < kBM && tid < nvalid) {
+            const int r = tid;
+            uint32_t mx = 0;
+#pragma unroll 8
+            for (int c = 0; c < kActN; ++c) mx = max(mx, __float_as_uint(ft[c * kCS + r]) & 0x7FFFFFFFu);
+            const float amax = __uint_as_float(mx);
+            float scale, inv;
+            block_scale<true>(amax > 0x1p-100f ? amax : 0x1p-100f, scale, inv);
+            uint8_t* dst = a.act + (size_t)(row0 + r) * a.I + n0;
+#pragma unroll 2
+            for (int c0 = 0; c0 < kActN; c0 += 16) {
+                u32x4 q;
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int row = 64 * wr + 16 * r + 4 * g + i;
-                const float amax = __uint_as_float(max(amx[row], amx[kBM + row]));
-                const float aa = amax > 0x1p-100f ? amax : 0x1p-100f;
-                float scale, inv;
-                block_scale<true>(aa, scale, inv);
-                const uint32_t q = pack_e4m3x4(av[r][0][i] * inv, av[r][1][i] * inv, av[r][2][i] * inv,
-                                               av[r][3][i] * inv);
-#pragma unroll
-                for (int c = 0; c < 4; ++c) tile[row * kTS + 64 * wc + 16 * c + lr] = (uint8_t)(q >> (8 * c));
-                if (wc == 0 && lr == 0 && row < nvalid) a.act_s[(size_t)(row0 + row) * SI + n0 / kBK] = scale;
+                for (int j = 0; j < 4; ++j) {
+                    const float* p = ft + (c0 + 4 * j) * kCS + r;
+                    q[j] = pack_e4m3x4(p[0] * inv, p[kCS] * inv, p[2 * kCS] * inv, p[3 * kCS] * inv);
+                }
+                *(u32x4*)(dst + c0) = q;
             }
-        __syncthreads();
-        for (int i = tid; i < kBM * 8; i += kThreads) {
-            const int r = i >> 3, c = i & 7;
-            if (r < nvalid)
-                *(u32x4*)(a.act + (size_t)(row0 + r) * a.I + n0 + c * 16) = *(const u32x4*)(tile + r * kTS + c * 16);
+            a.act_s[(size_t)(row0 + r) * (a.I / kBK) + n0 / kBK] = scale;
         }
     } else {
         // ---- BF16 output tile [kBM][256 + 8], staged for 16-byte stores ------
-        // (rows padded by 16 bytes: the four rows a wave writes at once fall
-        // in different LDS banks; the tile may run into the scale area, which
-        // is no longer needed)
+        // (the tile may run into the scale area, which is no longer needed)
         constexpr int kTS = kBR + 8;
-        uint16_t* tile = (uint16_t*)stage;
+        uint16_t* tile = (uint16_t*)ring;
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
+        for (int t = 0; t < TM; ++t)
 #pragma unroll
-            for (int c = 0; c < 8; ++c)
+            for (int u = 0; u < 4; ++u)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int row = 64 * wr + 16 * r + 4 * g + i, col = 128 * wc + 16 * c + lr;
-                    const __bf16 b = (__bf16)acc[r][c][i];
+                for (int i = 0; i < 16; ++i) {
+                    const int row = 32 * TM * wr + 32 * t + 8 * (i >> 2) + 4 * g + (i & 3);
+                    const int col = 128 * wc + 32 * u + m;
+                    const __bf16 b = (__bf16)acc[t][u][i];
                     tile[row * kTS + col] = __builtin_bit_cast(uint16_t, b);
                 }
         __syncthreads();
@@ -335,53 +429,52 @@ __global__ __launch_bounds__(Tile<WM>::kThreads) void mlp_kernel(MlpArgs a) {
     }
 }
 
-// Dynamic LDS: the stages, the scales and the tile prefix; at least the
+// Dynamic LDS: the ring, the scales and the tile prefix; at least the
 // epilogue's staging tile, which reuses the same bytes from the start.
-template <int WM>
+template <int TM>
 size_t lds_bytes_for(int K, int E) {
-    using TL = Tile<WM>;
-    const int KB = K / kBK;
-    const size_t loop = TL::kStages * (size_t)TL::kStageBytes + (((size_t)TL::kBM * KB + 2 * KB + 15) & ~(size_t)15) +
-                        4 * (2 * (size_t)E + 1);
-    const size_t up_tile = 4096 + (size_t)TL::kBM * (kActN + 16);
+    using TL = Tile<TM>;
+    const size_t KB = (size_t)K / kBK;
+    const size_t loop = 2 * (size_t)TL::kStageBytes + 4 * (KB * 64 + 2 * KB) + 4 * (2 * (size_t)E + 1);
+    const size_t up_tile = (size_t)kActN * (TL::kBM + 4) * 4;
     const size_t down_tile = (size_t)TL::kBM * (kBR + 8) * 2;
-    return loop > up_tile ? (loop > down_tile ? loop : down_tile) : (up_tile > down_tile ? up_tile : down_tile);
+    const size_t r = loop > up_tile ? loop : up_tile;
+    return r > down_tile ? r : down_tile;
 }
 
 // 256-row tiles when experts average at least 512 rows, else 128-row tiles.
-int pick_wm(int N, int E) { return (long long)N >= 512LL * E ? 4 : 2; }
+int pick_tm(int N, int E) { return (long long)N >= 512LL * E ? 4 : 2; }
 
-template <bool UP, int WM>
+template <bool UP, int TM>
 hipError_t launch_mlp(const MlpArgs& a, hipStream_t s) {
-    const size_t lds = lds_bytes_for<WM>(a.K, a.E);
+    const size_t lds = lds_bytes_for<TM>(a.K, a.E);
     const unsigned gx = UP ? (unsigned)(a.I / kActN) : (unsigned)((a.WR + kBR - 1) / kBR);
-    const unsigned gy = (unsigned)(a.N / Tile<WM>::kBM + a.E);  // >= sum over experts of ceil(rows / BM)
+    const unsigned gy = (unsigned)(a.N / Tile<TM>::kBM + a.E);  // >= sum over experts of ceil(rows / BM)
     if (gx == 0 || gy == 0) return hipSuccess;
-    hipLaunchKernelGGL((mlp_kernel<UP, WM>), dim3(gx, gy), dim3(Tile<WM>::kThreads), lds, s, a);
+    hipLaunchKernelGGL((mlp_kernel<UP, TM>), dim3(gx, gy), dim3(kThreads), lds, s, a);
     return hipGetLastError();
 }
 
 template <bool UP>
 hipError_t launch_pick(const MlpArgs& a, hipStream_t s) {
-    return pick_wm(a.N, a.E) == 4 ? launch_mlp<UP, 4>(a, s) : launch_mlp<UP, 2>(a, s);
+    return pick_tm(a.N, a.E) == 4 ? launch_mlp<UP, 4>(a, s) : launch_mlp<UP, 2>(a, s);
 }
 
 }  // namespace
 
 size_t expert_mlp_lds_bytes(int N, int K, int E) {
-    return pick_wm(N, E) == 4 ? lds_bytes_for<4>(K, E) : lds_bytes_for<2>(K, E);
+    return pick_tm(N, E) == 4 ? lds_bytes_for<4>(K, E) : lds_bytes_for<2>(K, E);
 }
 
 // Raises the kernels' dynamic-LDS limit above the 64 KiB default (the
 // attribute belongs to the function on the current device).
 hipError_t prepare_expert_mlp(bool up, int N, int K, int E) {
-    const int wm = pick_wm(N, E);
+    const int tm = pick_tm(N, E);
     const size_t lds = expert_mlp_lds_bytes(N, K, E);
-    const void* f = up ? (wm == 4 ? (const void*)mlp_kernel<true, 4> : (const void*)mlp_kernel<true, 2>)
-                       : (wm == 4 ? (const void*)mlp_kernel<false, 4> : (const void*)mlp_kernel<false, 2>);
+    const void* f = up ? (tm == 4 ? (const void*)mlp_kernel<true, 4> : (const void*)mlp_kernel<true, 2>)
+                       : (tm == 4 ? (const void*)mlp_kernel<false, 4> : (const void*)mlp_kernel<false, 2>);
     return hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
 }
-
 hipError_t launch_expert_up(const int32_t* cnt_e, const int32_t* off_e, const uint8_t* x, const float* xs,
                             const uint8_t* w1, const float* w1s, uint8_t* act, float* act_s, int N, int H, int I,
                             int E, int C, hipStream_t stream) {

@@ -334,6 +334,8 @@ moe_status moe_expert_up(const moe_mlp_cfg* c, const int32_t* cnt_e, const int32
     const moe_status st = check_mlp_cfg(c, "expert_up");
     if (st != MOE_OK) return st;
     if (c->hidden > 8192) return fail(MOE_ERR_INVALID, "expert_up: hidden %d above 8192", c->hidden);
+    if ((int64_t)c->num_rows * c->hidden > (1ll << 32))
+        return fail(MOE_ERR_UNSUPPORTED, "expert_up: num_rows*hidden above 2^32");
     if (c->num_rows == 0) return ok();
     if (!cnt_e || (c->capacity == 0 && !off_e) || !x || !x_scales || !w1 || !w1_scales || !act || !act_scales)
         return fail(MOE_ERR_INVALID, "expert_up: NULL array");
@@ -354,6 +356,8 @@ moe_status moe_expert_down(const moe_mlp_cfg* c, const int32_t* cnt_e, const int
                            void* stream) {
     const moe_status st = check_mlp_cfg(c, "expert_down");
     if (st != MOE_OK) return st;
+    if ((int64_t)c->num_rows * c->inter > (1ll << 32))
+        return fail(MOE_ERR_UNSUPPORTED, "expert_down: num_rows*inter above 2^32");
     if (c->num_rows == 0) return ok();
     if (!cnt_e || (c->capacity == 0 && !off_e) || !act || !act_scales || !w2 || !w2_scales || !y)
         return fail(MOE_ERR_INVALID, "expert_down: NULL array");

@@ -340,7 +340,9 @@ moe_status moe_route_dispatch(const moe_route_cfg* route, const moe_layout_cfg* 
 /*   act uint8 [N,I], act_scales fp32 [N,I/128], w2 uint8 [E,H,I],           */
 /*   w2_scales fp32 [E,H/128,I/128] in; y bf16 [N,H] out.                   */
 /* Limits: H and I multiples of 128, H <= 8192 for up, I <= 8192,           */
-/* 1 <= E <= 512.  Code arrays and y 16-byte aligned.                       */
+/* 1 <= E <= 512 (MOE_ERR_INVALID otherwise); N*H (up) and N*I (down) at    */
+/* most 2^32, so that a row offset fits in 32 bits (MOE_ERR_UNSUPPORTED     */
+/* otherwise).  Code arrays and y 16-byte aligned.                          */
 /* ------------------------------------------------------------------------ */
 typedef struct {
     int32_t num_rows;     /* N: rows of the receive buffer */

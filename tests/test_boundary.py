@@ -208,3 +208,14 @@ def test_expert_up_rejects_hidden_above_8192():
 @pytest.mark.parametrize("fn,n_args", [("moe_expert_up", 9), ("moe_expert_down", 8)])
 def test_expert_mlp_zero_rows_is_noop(fn, n_args):
     assert _mlp(fn, (0, 7168, 2048, 8, 0), n_args) == moe.MOE_OK
+
+
+@pytest.mark.parametrize("fn,n_args,vals", [
+    ("moe_expert_up", 9, (600000, 8192, 2048, 8, 0)),     # N*H above 2^32
+    ("moe_expert_down", 8, (600000, 7168, 8192, 8, 0)),   # N*I above 2^32
+])
+def test_expert_mlp_32bit_offsets(fn, n_args, vals):
+    """Row offsets inside the kernels are 32-bit: larger receive buffers are
+    refused before any array is looked at."""
+    assert _mlp(fn, vals, n_args) == moe.MOE_ERR_UNSUPPORTED
+    assert moe.lib().moe_last_error()

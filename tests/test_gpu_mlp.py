@@ -5,10 +5,13 @@ Both sides read the same FP8 codes and power-of-two scales.  The GPU sums in
 fp32 on the matrix cores, the oracle in double, so results are compared
 within bounds derived from the arithmetic:
   up:   |dq_gpu - act| <= 2^-4 (|act| + d) + 2^-10 s_gpu + d, where
-        d = 1.1 |u| dh + |silu(g)| dh + 2^-20 |act| bounds the fp32 error of
-        the activation (dh = K 2^-24 sum_k |x_k w_k|, the worst case of an
-        fp32 sum of K terms) and the rest is the E4M3 rounding of a value
-        with power-of-two scale s (half a step, 2^-10 s below the normals);
+        d = 1.1 |u| dh + |silu(g)| dh + (|g| 2^-24 + 2^-20) |act| bounds the
+        fp32 error of the activation (dh = K 2^-24 sum_k |x_k w_k|, the worst
+        case of an fp32 sum of K terms; the last term covers SwiGLU itself,
+        evaluated with the hardware exp2 and reciprocal, 1 ulp each, on the
+        rounded product -g log2(e)) and the rest is the E4M3 rounding of a
+        value with power-of-two scale s (half a step, 2^-10 s below the
+        normals);
         scales must agree except where the fp32 row maximum crossed a power
         of two (then by exactly a factor 2);
   down: |y_gpu - y| <= 2^-8 |y| + 2^-8 |y_gpu| + 2 K 2^-24 sum_k |a_k w_k|
@@ -81,7 +84,7 @@ def check_up(x, xs, w1, w1s, start, count, act_g, act_s_g, rows):
         g, u = h[:I], h[I:]
         silu = g / (1.0 + np.exp(-g))
         a = f64[r]
-        d = 1.1 * np.abs(u) * dh[:I] + np.abs(silu) * dh[I:] + 2.0 ** -20 * np.abs(a)
+        d = 1.1 * np.abs(u) * dh[:I] + np.abs(silu) * dh[I:] + (np.abs(g) * 2.0 ** -24 + 2.0 ** -20) * np.abs(a)
         s_g = np.repeat(act_s_g[r].astype(np.float64), 128)
         dq = E4M3[act_g[r]] * s_g
         bound = 2.0 ** -4 * (np.abs(a) + d) + 2.0 ** -10 * s_g + d
