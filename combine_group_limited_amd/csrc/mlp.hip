@@ -80,6 +80,7 @@ struct MlpArgs {
     float* act_s;          // up: [N, I/128]
     uint16_t* y;           // down: [N, WR] bf16
     int N, K, WR, E, C, I;
+    int gx, rw, rh, nrect;  // tile grid width (column tiles) and the XCD rectangles
 };
 
 __device__ __forceinline__ uint32_t e8m0(float s) { return (__float_as_uint(s) >> 23) & 0xFFu; }
@@ -163,6 +164,20 @@ __global__ __launch_bounds__(kThreads) void mlp_kernel(MlpArgs a) {
     const int lane = tid & 63, w = tid >> 6, wr = w >> 1, wc = w & 1;
     const int m = lane & 31, g = lane >> 5;
 
+    // Tile order: the chip deals consecutive blocks to its 8 XCDs in turn and
+    // each XCD has its own L2, so the 32 blocks an XCD runs at once are given
+    // one rh x rw rectangle of (row slot, column) tiles: 4 x 8 for up shares
+    // each A panel among 8 blocks and each weight panel among 4 in one L2.
+    int slot, col;
+    {
+        const int b = blockIdx.x, x = b & 7, i = b >> 3;
+        const int R = (i >> 5) * 8 + x, p = i & 31;
+        if (R >= a.nrect) return;  // block-uniform
+        const int rpr = a.gx / a.rw;  // rectangles per rectangle row
+        slot = (R / rpr) * a.rh + p / a.rw;
+        col = (R % rpr) * a.rw + p % a.rw;
+    }
+
     // ---- which expert and row tile this block computes --------------------
     for (int e = tid; e < a.E; e += kThreads) {
         int st;
@@ -170,7 +185,6 @@ __global__ __launch_bounds__(kThreads) void mlp_kernel(MlpArgs a) {
     }
     __syncthreads();
     block_exclusive_scan<kThreads>(tot, tpref, a.E, 0);  // ends with a barrier
-    const int slot = blockIdx.y;
     if (slot >= tpref[a.E]) return;  // block-uniform
     int lo = 0, hi = a.E - 1;        // the expert e with tpref[e] <= slot < tpref[e+1]
     while (lo < hi) {
@@ -182,7 +196,7 @@ __global__ __launch_bounds__(kThreads) void mlp_kernel(MlpArgs a) {
     const int cnt = rows_of(a, e, start);
     const int row0 = start + (slot - tpref[e]) * kBM;
     const int nvalid = min(kBM, start + cnt - row0);
-    const int n0 = blockIdx.x * (UP ? kActN : kBR);
+    const int n0 = col * (UP ? kActN : kBR);
 
     // ---- K loop -----------------------------------------------------------
     // One 128-deep stage (kBM rows of A and 256 weight rows, 128 bytes each)
@@ -448,10 +462,15 @@ int pick_tm(int N, int E) { return (long long)N >= 512LL * E ? 4 : 2; }
 template <bool UP, int TM>
 hipError_t launch_mlp(const MlpArgs& a, hipStream_t s) {
     const size_t lds = lds_bytes_for<TM>(a.K, a.E);
-    const unsigned gx = UP ? (unsigned)(a.I / kActN) : (unsigned)((a.WR + kBR - 1) / kBR);
-    const unsigned gy = (unsigned)(a.N / Tile<TM>::kBM + a.E);  // >= sum over experts of ceil(rows / BM)
-    if (gx == 0 || gy == 0) return hipSuccess;
-    hipLaunchKernelGGL((mlp_kernel<UP, TM>), dim3(gx, gy), dim3(kThreads), lds, s, a);
+    MlpArgs g = a;
+    g.gx = UP ? a.I / kActN : (a.WR + kBR - 1) / kBR;
+    const int gy = a.N / Tile<TM>::kBM + a.E;  // >= sum over experts of ceil(rows / BM)
+    if (g.gx == 0 || gy == 0) return hipSuccess;
+    g.rw = g.gx % 8 == 0 ? 8 : g.gx % 4 == 0 ? 4 : g.gx % 2 == 0 ? 2 : 1;
+    g.rh = 32 / g.rw;
+    g.nrect = (gy + g.rh - 1) / g.rh * (g.gx / g.rw);
+    const unsigned blocks = (unsigned)((g.nrect + 7) / 8 * 8 * 32);  // every rectangle gets its 32 blocks
+    hipLaunchKernelGGL((mlp_kernel<UP, TM>), dim3(blocks), dim3(kThreads), lds, s, g);
     return hipGetLastError();
 }
 
