@@ -204,6 +204,14 @@ def backward_main(args, wl, moe, torch, dev, sets, hev, stream):
         "dispatch_backward_gbps": round(b["dispatch_backward"] / (db_us * 1e-6) / 1e9, 1),
         "pct_of_hbm_peak": round(100 * tot / ((cb_us + db_us) * 1e-6) / 1e9 / HBM_PEAK_GBPS, 2),
     }
+    # the dominant kernel is combine's backward (gather y, write grad_y)
+    achieved = b["combine_backward"] / (cb_us * 1e-6) / 1e9
+    digest = source_digest("backward.hip", "moe_device.hpp")
+    res["roofline"] = {"kernel": "combine_backward", "bound": "hbm", "achieved": round(achieved, 1),
+                       "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                       "traffic": load_traffic("combine_backward", digest, wl.name),
+                       "algorithmic_bytes": b["combine_backward"], "avg_launch_us": round(cb_us, 2),
+                       "source_digest": digest}
     print(json.dumps(res), flush=True)
 
 
