@@ -148,15 +148,19 @@ __device__ __forceinline__ void mma_tile(f32x16 (&acc)[TM][4], const Frag<TM>& f
     else if constexpr (T + 1 < TM) mma_tile<UP, TM, T + 1, 0>(acc, f);
 }
 
-template <bool UP, int TM>
+// NR: stage buffers in the ring (2, or 3 for 128-row tiles when it fits:
+// their stages are smaller and the kernel streams weights, so a second stage
+// in flight pays).
+template <bool UP, int TM, int NR>
 __global__ __launch_bounds__(kThreads) void mlp_kernel(MlpArgs a) {
     using TL = Tile<TM>;
     constexpr int kBM = TL::kBM, kStageBytes = TL::kStageBytes, kCopies = TL::kCopies;
+    constexpr int kSW = TM > 2 ? 4 : 2;  // bytes per row-scale word (one byte per row tile)
     extern __shared__ __align__(16) uint8_t smem[];
-    uint8_t* ring = smem;                                          // [2][kStageBytes]
+    uint8_t* ring = smem;                                          // [NR][kStageBytes]
     const int KB = a.K / kBK;
-    uint32_t* a_sc = (uint32_t*)(smem + 2 * kStageBytes);          // [KB][2][32]: byte t = row tile t
-    uint32_t* w_sc = a_sc + KB * 64;                               // [KB][2]
+    uint8_t* a_sc = smem + NR * kStageBytes;                       // [KB][2][32] words: byte t = row tile t
+    uint32_t* w_sc = (uint32_t*)(a_sc + KB * 64 * kSW);            // [KB][2]
     int32_t* tot = (int32_t*)(w_sc + 2 * KB);                      // [E]
     int32_t* tpref = tot + a.E;                                    // [E+1]
 
@@ -260,7 +264,9 @@ __global__ __launch_bounds__(kThreads) void mlp_kernel(MlpArgs a) {
             const i32x4 hi4 = *(const i32x4*)(sB + swz(brow[u], c0 + 1));
             f.b[u] = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
         }
-        f.sa = a_sc[(st * 2 + wr) * 32 + m];
+        const int wi = (st * 2 + wr) * 32 + m;
+        if constexpr (kSW == 4) f.sa = ((const uint32_t*)a_sc)[wi];
+        else f.sa = ((const uint16_t*)a_sc)[wi];
         f.sb = w_sc[st * 2 + wc];
     };
 
@@ -272,21 +278,22 @@ __global__ __launch_bounds__(kThreads) void mlp_kernel(MlpArgs a) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) acc[t][u][i] = 0.0f;
 
-    // Stage protocol (two buffers; stage S lives in buffer S % 2).  Each
+    // Stage protocol (NR buffers; stage S lives in buffer S % NR).  Each
     // stage is two MFMA halves.  During half 0 of S the wave reads the
     // fragments of half 1 of S; then every wave waits until its copies of
-    // stage S+1 have landed (they are the only ones outstanding) and its own
-    // reads are done, and meets the others at a bare barrier: S+1 is now
-    // visible to all and buffer S % 2 is free, so stage S+2 is issued into
-    // it, and half 1 of S runs while half 0 of S+1 is read.  One barrier per
-    // stage; a stage's copies have a whole stage of MFMAs to land.
+    // stage S+1 have landed (only the NR - 2 later stages may still be in
+    // flight; s_waitcnt vmcnt counts copies in issue order) and its own reads
+    // are done, and meets the others at a bare barrier: S+1 is now visible to
+    // all and buffer S % NR is free, so stage S+NR is issued into it, and
+    // half 1 of S runs while half 0 of S+1 is read.  One barrier per stage; a
+    // stage's copies have NR - 1 stages of MFMAs to land.
     Frag<TM> f0, f1;
-    issue(0, 0);
-    issue(1, 1);
+#pragma unroll
+    for (int q = 0; q < NR; ++q) issue(q, q);
     // ---- scales of the whole K range, as E8M0 bytes ------------------------
-    // Issued after the first slices' copies so both latencies overlap.  a_sc
-    // word (kb, wr, m) holds the scales of rows 32*TM*wr + 32t + m (t < TM)
-    // in byte t (bytes >= TM are never read).
+    // Issued after the first stages' copies so both latencies overlap.  a_sc
+    // word (kb, wr, m) (kSW bytes) holds the scales of rows 32*TM*wr + 32t + m
+    // (t < TM) in byte t.
     {
         // the block's kBM x KB scales are one contiguous run of a.as (reads
         // past the array's end take its last element: those rows are never
@@ -304,8 +311,7 @@ __global__ __launch_bounds__(kThreads) void mlp_kernel(MlpArgs a) {
 #pragma unroll
             for (int j = 0; j < 16; ++j) {
                 if (tid + (j0 + j) * kThreads < n)
-                    ((uint8_t*)a_sc)[kb * 256 + ((r / (32 * TM)) * 32 + (r & 31)) * 4 + (r / 32) % TM] =
-                        (uint8_t)e8m0(v[j]);
+                    a_sc[(kb * 64 + (r / (32 * TM)) * 32 + (r & 31)) * kSW + (r / 32) % TM] = (uint8_t)e8m0(v[j]);
                 r += dq;
                 kb += dr;
                 if (kb >= KB) {
@@ -329,7 +335,7 @@ __global__ __launch_bounds__(kThreads) void mlp_kernel(MlpArgs a) {
         w_sc[i] = v;
     }
     __syncthreads();  // scales in LDS
-    wait_vm<0>();     // both stages too (the scale loads were issued after them)
+    wait_vm<0>();     // the first stages too (the scale loads were issued after them)
     bare_barrier();
     read(f0, 0, 0, 0);
 
@@ -338,7 +344,7 @@ __global__ __launch_bounds__(kThreads) void mlp_kernel(MlpArgs a) {
     constexpr int kVm = (kCopies + kM - 1) / kM;           // copies per MFMA slot
     int st = 0;
     for (; st + 1 < KB; ++st) {
-        const int b = st & 1;
+        const int b = st % NR;
         read(f1, st, b, 1);
         mma_tile<UP, TM, 0, 0>(acc, f0);
 #pragma unroll
@@ -347,10 +353,10 @@ __global__ __launch_bounds__(kThreads) void mlp_kernel(MlpArgs a) {
             __builtin_amdgcn_sched_group_barrier(0x100, kDs, 0);  // LDS reads
         }
         __builtin_amdgcn_sched_barrier(0);
-        wait_vm<0, true>();
+        wait_vm<(NR - 2) * kCopies, true>();
         bare_barrier();
-        issue(st + 2, b);
-        read(f0, st + 1, b ^ 1, 0);
+        issue(st + NR, b);
+        read(f0, st + 1, (st + 1) % NR, 0);
         mma_tile<UP, TM, 0, 0>(acc, f1);
 #pragma unroll
         for (int i = 0; i < kM; ++i) {
@@ -361,7 +367,7 @@ __global__ __launch_bounds__(kThreads) void mlp_kernel(MlpArgs a) {
         __builtin_amdgcn_sched_barrier(0);
     }
     // the last stage
-    read(f1, st, st & 1, 1);
+    read(f1, st, st % NR, 1);
     mma_tile<UP, TM, 0, 0>(acc, f0);
     wait_vm<0, true>();
     mma_tile<UP, TM, 0, 0>(acc, f1);
@@ -451,22 +457,28 @@ __global__ __launch_bounds__(kThreads) void mlp_kernel(MlpArgs a) {
 // Dynamic LDS: the ring, the scales and the tile prefix; at least the
 // epilogue's staging tile, which reuses the same bytes from the start.
 template <int TM>
-size_t lds_bytes_for(int K, int E) {
+size_t lds_bytes_for(int K, int E, int nr) {
     using TL = Tile<TM>;
-    const size_t KB = (size_t)K / kBK;
-    const size_t loop = 2 * (size_t)TL::kStageBytes + 4 * (KB * 64 + 2 * KB) + 4 * (2 * (size_t)E + 1);
+    const size_t KB = (size_t)K / kBK, sw = TM > 2 ? 4 : 2;
+    const size_t loop = nr * (size_t)TL::kStageBytes + KB * 64 * sw + 4 * (2 * KB) + 4 * (2 * (size_t)E + 1);
     const size_t up_tile = (size_t)kActN * (TL::kBM + 4) * 4;
     const size_t down_tile = (size_t)TL::kBM * (kBR + 8) * 2;
     const size_t r = loop > up_tile ? loop : up_tile;
     return r > down_tile ? r : down_tile;
 }
 
-// 256-row tiles when experts average at least 512 rows, else 128-row tiles.
-int pick_tm(int N, int E) { return (long long)N >= 512LL * E ? 4 : 2; }
+constexpr size_t kMaxLds = 160 * 1024;  // LDS per workgroup on gfx950
 
-template <bool UP, int TM>
+// 256-row tiles when experts average at least 512 rows, else 128-row tiles.
+// (64-row tiles for decode-sized batches, to bring more CUs to the weight
+// stream, were measured slower: each weight panel then enters two CUs.)
+int pick_tm(int N, int E) { return (long long)N >= 512LL * E ? 4 : 2; }
+// three stage buffers for 128-row tiles when they fit, else two
+int pick_nr(int tm, int K, int E) { return tm == 2 && lds_bytes_for<2>(K, E, 3) <= kMaxLds ? 3 : 2; }
+
+template <bool UP, int TM, int NR>
 hipError_t launch_mlp(const MlpArgs& a, hipStream_t s) {
-    const size_t lds = lds_bytes_for<TM>(a.K, a.E);
+    const size_t lds = lds_bytes_for<TM>(a.K, a.E, NR);
     MlpArgs g = a;
     g.gx = UP ? a.I / kActN : (a.WR + kBR - 1) / kBR;
     const int gy = a.N / Tile<TM>::kBM + a.E;  // >= sum over experts of ceil(rows / BM)
@@ -475,28 +487,40 @@ hipError_t launch_mlp(const MlpArgs& a, hipStream_t s) {
     g.rh = 32 / g.rw;
     g.nrect = (gy + g.rh - 1) / g.rh * (g.gx / g.rw);
     const unsigned blocks = (unsigned)((g.nrect + 7) / 8 * 8 * 32);  // every rectangle gets its 32 blocks
-    hipLaunchKernelGGL((mlp_kernel<UP, TM>), dim3(blocks), dim3(kThreads), lds, s, g);
+    hipLaunchKernelGGL((mlp_kernel<UP, TM, NR>), dim3(blocks), dim3(kThreads), lds, s, g);
     return hipGetLastError();
 }
 
 template <bool UP>
 hipError_t launch_pick(const MlpArgs& a, hipStream_t s) {
-    return pick_tm(a.N, a.E) == 4 ? launch_mlp<UP, 4>(a, s) : launch_mlp<UP, 2>(a, s);
+    const int tm = pick_tm(a.N, a.E), nr = pick_nr(tm, a.K, a.E);
+    if (tm == 4) return launch_mlp<UP, 4, 2>(a, s);
+    return nr == 3 ? launch_mlp<UP, 2, 3>(a, s) : launch_mlp<UP, 2, 2>(a, s);
+}
+
+template <bool UP>
+const void* kernel_for(int tm, int nr) {
+    if (tm == 4) return (const void*)mlp_kernel<UP, 4, 2>;
+    return nr == 3 ? (const void*)mlp_kernel<UP, 2, 3> : (const void*)mlp_kernel<UP, 2, 2>;
+}
+
+size_t lds_bytes_tm(int tm, int K, int E, int nr) {
+    return tm == 4 ? lds_bytes_for<4>(K, E, nr) : lds_bytes_for<2>(K, E, nr);
 }
 
 }  // namespace
 
 size_t expert_mlp_lds_bytes(int N, int K, int E) {
-    return pick_tm(N, E) == 4 ? lds_bytes_for<4>(K, E) : lds_bytes_for<2>(K, E);
+    const int tm = pick_tm(N, E);
+    return lds_bytes_tm(tm, K, E, pick_nr(tm, K, E));
 }
 
 // Raises the kernels' dynamic-LDS limit above the 64 KiB default (the
 // attribute belongs to the function on the current device).
 hipError_t prepare_expert_mlp(bool up, int N, int K, int E) {
-    const int tm = pick_tm(N, E);
-    const size_t lds = expert_mlp_lds_bytes(N, K, E);
-    const void* f = up ? (tm == 4 ? (const void*)mlp_kernel<true, 4> : (const void*)mlp_kernel<true, 2>)
-                       : (tm == 4 ? (const void*)mlp_kernel<false, 4> : (const void*)mlp_kernel<false, 2>);
+    const int tm = pick_tm(N, E), nr = pick_nr(tm, K, E);
+    const size_t lds = lds_bytes_tm(tm, K, E, nr);
+    const void* f = up ? kernel_for<true>(tm, nr) : kernel_for<false>(tm, nr);
     return hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
 }
 hipError_t launch_expert_up(const int32_t* cnt_e, const int32_t* off_e, const uint8_t* x, const float* xs,

@@ -199,6 +199,9 @@ MLP_WORKLOADS = {
     "mlp_rank": MlpWorkload("mlp_rank", N=32768, H=7168, I=2048, E=8),
     # the single-GPU receive buffer of dsv3_prefill: 256 experts, 32768 rows
     "mlp_all": MlpWorkload("mlp_all", N=32768, H=7168, I=2048, E=256),
+    # one rank at decode: 32 ranks x 128 tokens x top-8 / 32 = 1024 rows over the
+    # 8 local experts (~128 each): the weights dominate the bytes
+    "mlp_decode": MlpWorkload("mlp_decode", N=1024, H=7168, I=2048, E=8),
 }
 
 
