@@ -26,14 +26,14 @@
 // MFMA tiles (TM = 4: 256 accumulators per lane, one wave per SIMD).  Up:
 // the block's weight rows are 128 gate rows and the matching 128 up rows, and
 // wave wc takes gate rows 64wc.. and the same up rows, so SwiGLU pairs
-// registers of one lane; down: 256 output columns.  The K loop stages
-// 128-deep slices of both operands (whole 128-byte lines per row) in two LDS
-// buffers filled by direct global->LDS copies; 16-byte chunks are
-// XOR-swizzled by row so fragment reads are conflict-free.  Each stage is
-// computed as two 64-deep halves with two register sets, so the fragments of
-// the next half are read while the MFMAs of the current one run, and one
-// barrier per stage publishes the next stage and frees a buffer for the one
-// after.  Expert row ranges come from the layout (off_e and cnt_e, or e*C and
+// registers of one lane; down: 256 output columns.  The K loop moves
+// 128-deep stages of both operands (whole 128-byte lines per row) through
+// two LDS buffers (three for 128-row tiles) filled by direct global->LDS
+// copies; 16-byte chunks are XOR-swizzled by row so fragment reads are
+// conflict-free.  Each stage is computed as two 64-deep halves with two
+// register sets, so the fragments of the next half are read while the MFMAs
+// of the current one run, and one barrier per stage publishes the next stage
+// and frees a buffer for a later one.  Expert row ranges come from the layout (off_e and cnt_e, or e*C and
 // min(cnt_e, C) when padded); each block finds its (expert, row tile) from
 // the per-expert tile counts, so the grid is sized without reading anything
 // back to the host.
@@ -106,7 +106,7 @@ __device__ __forceinline__ int rows_of(const MlpArgs& a, int e, int& start) {
 __device__ __forceinline__ int swz_key(int r) { return (r >> 1) & 7; }
 __device__ __forceinline__ int swz(int r, int c) { return r * kBK + ((c ^ swz_key(r)) << 4); }
 
-// Weight row (within the expert's [WR, K] matrix) staged at B-slice row r.
+// Weight row (within the expert's [WR, K] matrix) staged at B-stage row r.
 template <bool UP>
 __device__ __forceinline__ int wrow_of(const MlpArgs& a, int n0, int r) {
     if constexpr (UP) return r < kActN ? n0 + r : a.I + n0 + (r - kActN);
