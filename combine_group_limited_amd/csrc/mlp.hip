@@ -288,30 +288,84 @@ __global__ __launch_bounds__(kThreads) void mlp_kernel(MlpArgs a) {
     // half 1 of S runs while half 0 of S+1 is read.  One barrier per stage; a
     // stage's copies have NR - 1 stages of MFMAs to land.
     Frag<TM> f0, f1;
+
+    // ---- scales of the whole K range, as E8M0 bytes ------------------------
+    // a_sc word (kb, wr, m) (kSW bytes) holds the scales of rows 32*TM*wr +
+    // 32t + m (t < TM) in byte t.  The block's kBM x KB row scales are one
+    // contiguous run of a.as (reads past the array's end take its last
+    // element: those rows are never stored).  Their loads are issued before
+    // the first stages' copies: s_waitcnt vmcnt retires loads in issue order,
+    // so scale loads issued behind 128 KiB of copies would wait for all of
+    // them.  With KB a multiple of 4 and a 16-byte aligned run, sixteen
+    // 16-byte loads per thread cover 64 Ki scales per batch (K <= 32768 at
+    // 256-row tiles: one batch); otherwise single scales, sixteen at a time.
+    auto a_sc_put = [&](int r, int kb, float v) {
+        a_sc[(kb * 64 + (r / (32 * TM)) * 32 + (r & 31)) * kSW + (r / 32) % TM] = (uint8_t)e8m0(v);
+    };
+    const int n_sc = kBM * KB;
+    const float* src_sc = a.as + (size_t)row0 * KB;
+    const int last_sc = min(n_sc, (a.N - row0) * KB) - 1;
+    const bool vec_sc = (KB & 3) == 0 && ((reinterpret_cast<uintptr_t>(src_sc) & 15) == 0);
+    constexpr int kSV = 16;  // 16-byte scale loads per thread per batch
+    f32x4 sv[kSV];
+    if (vec_sc) {
+#pragma unroll
+        for (int j = 0; j < kSV; ++j) sv[j] = ((const f32x4*)src_sc)[min(tid + j * kThreads, last_sc >> 2)];
+    }
+    const int WRB = a.WR / kBK;
+    auto w_sc_load = [&](int i) -> uint32_t {
+        const int kb = i >> 1, which = i & 1;
+        if constexpr (UP) {  // byte 0 the gate block, byte 1 the up block (both wave columns)
+            const size_t base = (size_t)e * WRB * KB + kb;
+            return e8m0(a.ws[base + (size_t)(n0 / kBK) * KB]) | (e8m0(a.ws[base + (size_t)((a.I + n0) / kBK) * KB]) << 8);
+        } else {             // the wave column's 128 output rows
+            const int blk = min(n0 / kBK + which, WRB - 1);
+            return e8m0(a.ws[((size_t)e * WRB + blk) * KB + kb]);
+        }
+    };
+    float ws_raw0 = 0.0f, ws_raw1 = 0.0f;  // this thread's first w_sc entry, loaded early
+    if (tid < 2 * KB) {
+        const int kb = tid >> 1, which = tid & 1;
+        if constexpr (UP) {
+            const size_t base = (size_t)e * WRB * KB + kb;
+            ws_raw0 = a.ws[base + (size_t)(n0 / kBK) * KB];
+            ws_raw1 = a.ws[base + (size_t)((a.I + n0) / kBK) * KB];
+        } else {
+            ws_raw0 = a.ws[((size_t)e * WRB + min(n0 / kBK + which, WRB - 1)) * KB + kb];
+        }
+    }
+
 #pragma unroll
     for (int q = 0; q < NR; ++q) issue(q, q);
-    // ---- scales of the whole K range, as E8M0 bytes ------------------------
-    // Issued after the first stages' copies so both latencies overlap.  a_sc
-    // word (kb, wr, m) (kSW bytes) holds the scales of rows 32*TM*wr + 32t + m
-    // (t < TM) in byte t.
-    {
-        // the block's kBM x KB scales are one contiguous run of a.as (reads
-        // past the array's end take its last element: those rows are never
-        // stored): thread i takes elements i, i + 256, ..., sixteen loads in
-        // flight at a time; (row, kb) of each element is stepped, not divided
-        const int n = kBM * KB;
-        const float* src = a.as + (size_t)row0 * KB;
-        const int last = min(n, (a.N - row0) * KB) - 1;
+
+    if (vec_sc) {
+        // float4 f of the run holds scales 4f..4f+3: one row, four K blocks
+        for (int j0 = 0; j0 * kThreads * 4 < n_sc; j0 += kSV) {
+            if (j0 > 0) {
+#pragma unroll
+                for (int j = 0; j < kSV; ++j) sv[j] = ((const f32x4*)src_sc)[min(tid + (j0 + j) * kThreads, last_sc >> 2)];
+            }
+#pragma unroll
+            for (int j = 0; j < kSV; ++j) {
+                const int f4 = tid + (j0 + j) * kThreads;
+                if (4 * f4 < n_sc) {
+                    const int r = (4 * f4) / KB, kb = 4 * f4 - r * KB;
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) a_sc_put(r, kb + c, sv[j][c]);
+                }
+            }
+        }
+    } else {
+        // thread i takes elements i, i + 256, ...; (row, kb) is stepped
         const int dq = kThreads / KB, dr = kThreads - dq * KB;
         int r = tid / KB, kb = tid - r * KB;
-        for (int j0 = 0; j0 * kThreads < n; j0 += 16) {
+        for (int j0 = 0; j0 * kThreads < n_sc; j0 += 16) {
             float v[16];
 #pragma unroll
-            for (int j = 0; j < 16; ++j) v[j] = src[min(tid + (j0 + j) * kThreads, last)];
+            for (int j = 0; j < 16; ++j) v[j] = src_sc[min(tid + (j0 + j) * kThreads, last_sc)];
 #pragma unroll
             for (int j = 0; j < 16; ++j) {
-                if (tid + (j0 + j) * kThreads < n)
-                    a_sc[(kb * 64 + (r / (32 * TM)) * 32 + (r & 31)) * kSW + (r / 32) % TM] = (uint8_t)e8m0(v[j]);
+                if (tid + (j0 + j) * kThreads < n_sc) a_sc_put(r, kb, v[j]);
                 r += dq;
                 kb += dr;
                 if (kb >= KB) {
@@ -321,19 +375,11 @@ __global__ __launch_bounds__(kThreads) void mlp_kernel(MlpArgs a) {
             }
         }
     }
-    const int WRB = a.WR / kBK;
-    for (int i = tid; i < 2 * KB; i += kThreads) {
-        const int kb = i >> 1, which = i & 1;
-        uint32_t v;
-        if constexpr (UP) {  // byte 0 the gate block, byte 1 the up block (both wave columns)
-            const size_t base = (size_t)e * WRB * KB + kb;
-            v = e8m0(a.ws[base + (size_t)(n0 / kBK) * KB]) | (e8m0(a.ws[base + (size_t)((a.I + n0) / kBK) * KB]) << 8);
-        } else {             // the wave column's 128 output rows
-            const int blk = min(n0 / kBK + which, WRB - 1);
-            v = e8m0(a.ws[((size_t)e * WRB + blk) * KB + kb]);
-        }
-        w_sc[i] = v;
+    if (tid < 2 * KB) {
+        if constexpr (UP) w_sc[tid] = e8m0(ws_raw0) | (e8m0(ws_raw1) << 8);
+        else w_sc[tid] = e8m0(ws_raw0);
     }
+    for (int i = tid + kThreads; i < 2 * KB; i += kThreads) w_sc[i] = w_sc_load(i);
     __syncthreads();  // scales in LDS
     wait_vm<0>();     // the first stages too (the scale loads were issued after them)
     bare_barrier();
@@ -403,21 +449,26 @@ __global__ __launch_bounds__(kThreads) void mlp_kernel(MlpArgs a) {
                 }
         __syncthreads();
         if (tid < kBM && tid < nvalid) {
+            // the row's 128 values are read once into registers (up to 15
+            // LDS reads in flight per wave), then reduced and encoded
             const int r = tid;
+            float v[kActN];
+#pragma unroll
+            for (int c = 0; c < kActN; ++c) v[c] = ft[c * kCS + r];
             uint32_t mx = 0;
-#pragma unroll 8
-            for (int c = 0; c < kActN; ++c) mx = max(mx, __float_as_uint(ft[c * kCS + r]) & 0x7FFFFFFFu);
+#pragma unroll
+            for (int c = 0; c < kActN; ++c) mx = max(mx, __float_as_uint(v[c]) & 0x7FFFFFFFu);
             const float amax = __uint_as_float(mx);
             float scale, inv;
             block_scale<true>(amax > 0x1p-100f ? amax : 0x1p-100f, scale, inv);
             uint8_t* dst = a.act + (size_t)(row0 + r) * a.I + n0;
-#pragma unroll 2
+#pragma unroll
             for (int c0 = 0; c0 < kActN; c0 += 16) {
                 u32x4 q;
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    const float* p = ft + (c0 + 4 * j) * kCS + r;
-                    q[j] = pack_e4m3x4(p[0] * inv, p[kCS] * inv, p[2 * kCS] * inv, p[3 * kCS] * inv);
+                    const float* p = v + c0 + 4 * j;
+                    q[j] = pack_e4m3x4(p[0] * inv, p[1] * inv, p[2] * inv, p[3] * inv);
                 }
                 *(u32x4*)(dst + c0) = q;
             }
