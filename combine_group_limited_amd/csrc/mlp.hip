@@ -106,6 +106,9 @@ __device__ __forceinline__ int rows_of(const MlpArgs& a, int e, int& start) {
 __device__ __forceinline__ int swz_key(int r) { return (r >> 1) & 7; }
 __device__ __forceinline__ int swz(int r, int c) { return r * kBK + ((c ^ swz_key(r)) << 4); }
 
+// Row-scale word of K block kb for wave row / lane slot w (0..63).
+__device__ __forceinline__ int sc_word(int kb, int w) { return kb * 64 + w; }
+
 // Weight row (within the expert's [WR, K] matrix) staged at B-stage row r.
 template <bool UP>
 __device__ __forceinline__ int wrow_of(const MlpArgs& a, int n0, int r) {
@@ -159,7 +162,7 @@ __global__ __launch_bounds__(kThreads) void mlp_kernel(MlpArgs a) {
     extern __shared__ __align__(16) uint8_t smem[];
     uint8_t* ring = smem;                                          // [NR][kStageBytes]
     const int KB = a.K / kBK;
-    uint8_t* a_sc = smem + NR * kStageBytes;                       // [KB][2][32] words: byte t = row tile t
+    uint8_t* a_sc = smem + NR * kStageBytes;                       // [KB][64] words: byte t = row tile t
     uint32_t* w_sc = (uint32_t*)(a_sc + KB * 64 * kSW);            // [KB][2]
     int32_t* tot = (int32_t*)(w_sc + 2 * KB);                      // [E]
     int32_t* tpref = tot + a.E;                                    // [E+1]
@@ -264,7 +267,7 @@ __global__ __launch_bounds__(kThreads) void mlp_kernel(MlpArgs a) {
             const i32x4 hi4 = *(const i32x4*)(sB + swz(brow[u], c0 + 1));
             f.b[u] = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
         }
-        const int wi = (st * 2 + wr) * 32 + m;
+        const int wi = sc_word(st, wr * 32 + m);
         if constexpr (kSW == 4) f.sa = ((const uint32_t*)a_sc)[wi];
         else f.sa = ((const uint16_t*)a_sc)[wi];
         f.sb = w_sc[st * 2 + wc];
@@ -290,8 +293,8 @@ __global__ __launch_bounds__(kThreads) void mlp_kernel(MlpArgs a) {
     Frag<TM> f0, f1;
 
     // ---- scales of the whole K range, as E8M0 bytes ------------------------
-    // a_sc word (kb, wr, m) (kSW bytes) holds the scales of rows 32*TM*wr +
-    // 32t + m (t < TM) in byte t.  The block's kBM x KB row scales are one
+    // a_sc word sc_word(kb, 32 wr + m) (kSW bytes) holds the scales of rows
+    // 32*TM*wr + 32t + m (t < TM) in byte t.  The block's kBM x KB row scales are one
     // contiguous run of a.as (reads past the array's end take its last
     // element: those rows are never stored).  Their loads are issued before
     // the first stages' copies: s_waitcnt vmcnt retires loads in issue order,
@@ -300,7 +303,7 @@ __global__ __launch_bounds__(kThreads) void mlp_kernel(MlpArgs a) {
     // 16-byte loads per thread cover 64 Ki scales per batch (K <= 32768 at
     // 256-row tiles: one batch); otherwise single scales, sixteen at a time.
     auto a_sc_put = [&](int r, int kb, float v) {
-        a_sc[(kb * 64 + (r / (32 * TM)) * 32 + (r & 31)) * kSW + (r / 32) % TM] = (uint8_t)e8m0(v);
+        a_sc[sc_word(kb, (r / (32 * TM)) * 32 + (r & 31)) * kSW + (r / 32) % TM] = (uint8_t)e8m0(v);
     };
     const int n_sc = kBM * KB;
     const float* src_sc = a.as + (size_t)row0 * KB;
@@ -412,11 +415,14 @@ __global__ __launch_bounds__(kThreads) void mlp_kernel(MlpArgs a) {
         }
         __builtin_amdgcn_sched_barrier(0);
     }
-    // the last stage
+    // the last stage (kept in program order: interleaving its two halves
+    // with each other and the epilogue makes the register allocator spill)
     read(f1, st, st % NR, 1);
     mma_tile<UP, TM, 0, 0>(acc, f0);
+    __builtin_amdgcn_sched_barrier(0);
     wait_vm<0, true>();
     mma_tile<UP, TM, 0, 0>(acc, f1);
+    __builtin_amdgcn_sched_barrier(0);
     __syncthreads();  // every copy has landed (waited above); the ring is reused below
 
 
