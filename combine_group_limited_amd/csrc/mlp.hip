@@ -384,7 +384,9 @@ __global__ __launch_bounds__(kThreads) void mlp_kernel(MlpArgs a) {
     }
     for (int i = tid + kThreads; i < 2 * KB; i += kThreads) w_sc[i] = w_sc_load(i);
     __syncthreads();  // scales in LDS
-    wait_vm<0>();     // the first stages too (the scale loads were issued after them)
+    // stage 0 has landed (the later stages' copies may still be in flight:
+    // every other load was consumed above, and the loop waits for stage 1)
+    wait_vm<(NR - 1) * kCopies>();
     bare_barrier();
     read(f0, 0, 0, 0);
 
