@@ -225,6 +225,41 @@ def test_mlp_rank_full_size_sampled():
     run_mlp(wl, start, count, rows=np.array(sorted(rows), np.int32))
 
 
+@pytest.mark.parametrize("N,H,I,E", [(4096, 1024, 512, 2), (1100, 640, 256, 2)])
+def test_mlp_unaligned_scales_match_aligned(N, H, I, E):
+    """Row scales at a 4-byte offset take the single-scale preload instead of
+    the 16-byte loads; both layouts must give bit-identical act, act scales
+    and y (256-row and 128-row tiles)."""
+    wl = W.MlpWorkload("unal", N=N, H=H, I=I, E=E, seed=9)
+    say(f"[gpu] mlp unaligned scales {wl}")
+    start, count, _ = W.mlp_ranges(wl)
+    x, xs = W.gen_mlp_x(wl)
+    w1, w1s = W.gen_mlp_weights(wl, "w1")
+    w2, w2s = W.gen_mlp_weights(wl, "w2")
+    cnt, off = layout_arrays(start, count)
+
+    def shifted(a):
+        buf = torch.empty(a.size + 1, dtype=torch.float32, device=DEV)
+        v = buf[1:].view(a.shape)
+        v.copy_(dev(a))
+        assert v.data_ptr() % 16 == 4
+        return v
+
+    outs = []
+    for xs_d, act_sd in ((dev(xs), None), (shifted(xs), "shift")):
+        act = torch.full((N, I), 0xEE, dtype=torch.uint8, device=DEV)
+        act_s = torch.full((N, I // 128), -3.0, dtype=torch.float32, device=DEV)
+        if act_sd:
+            act_s = shifted(act_s.cpu().numpy())
+        moe.expert_up(dev(x), xs_d, dev(w1), dev(w1s), dev(cnt), dev(off), 0, act, act_s)
+        y = torch.full((N, H), 1234, dtype=torch.int16, device=DEV).view(torch.bfloat16)
+        moe.expert_down(act, act_s, dev(w2), dev(w2s), dev(cnt), dev(off), 0, y)
+        torch.cuda.synchronize()
+        outs.append((act.cpu().numpy(), act_s.cpu().numpy(), y.view(torch.int16).cpu().numpy()))
+    for a, b in zip(outs[0], outs[1]):
+        assert np.array_equal(a, b)
+
+
 def test_mlp_zero_rows_is_noop():
     cfg = moe.MlpCfg(0, 7168, 2048, 8, 0)
     assert moe.lib().moe_expert_up(cfg, None, None, None, None, None, None, None, None, None) == moe.MOE_OK
