@@ -50,7 +50,7 @@ def parse():
     ap.add_argument("--cpu-reps", type=int, default=0, help="oracle repetitions (0: about 10 s)")
     ap.add_argument("--direction", choices=["forward", "backward"], default="forward",
                     help="backward: time combine_backward -> dispatch_backward instead")
-    ap.add_argument("--stage", choices=["dispatch_combine", "mlp"], default="dispatch_combine",
+    ap.add_argument("--stage", choices=["dispatch_combine", "mlp", "layer"], default="dispatch_combine",
                     help="mlp: time the expert MLP (up + SwiGLU + FP8 requantisation, down) instead")
     ap.add_argument("--mlp-workload", default="mlp_rank", choices=sorted(W.MLP_WORKLOADS))
     ap.add_argument("--copy-calibration", action="store_true",
@@ -278,6 +278,92 @@ def mlp_cpu_baseline(wl, x, xs, w1, w1s, w2, w2s, start, count, rows: int = 4):
                       f"projections, {dt:.1f} s, single thread"}
 
 
+def layer_main(args, torch, moe, hev, dev):
+    """The MoE layer after routing on one rank's shape (16384 tokens x 7168,
+    top-2 of 8 experts, I 2048; 32768 receive rows): moe_layer_forward (one
+    launch) against the four calls moe_dispatch -> moe_expert_up ->
+    moe_expert_down -> moe_combine on the same inputs."""
+    T, H, I, E, k = 16384, 7168, 2048, 8, 2
+    wl = W.custom("layer_rank", T=T, H=H, E=E, G=1, g=1, k=k, score="sigmoid", R=E, dtype="fp8")
+    mw = W.MlpWorkload("layer_rank_mlp", N=1, H=H, I=I, E=E, seed=7)
+    d = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    x = torch.from_numpy(W.gen_x(wl).view(np.int16)).to(dev).view(torch.bfloat16)
+    idx, w = moe.route_topk(d(W.gen_logits(wl)), 1, 1, k)
+    lay = moe.get_layout(idx, E, E)
+    N = lay.num_recv_rows
+    w1h, w1sh = W.gen_mlp_weights(mw, "w1")
+    w2h, w2sh = W.gen_mlp_weights(mw, "w2")
+    w1, w1s, w2, w2s = map(d, (w1h, w1sh, w2h, w2sh))
+    rx = torch.empty((N, H), dtype=torch.uint8, device=dev)
+    rs = torch.empty((N, H // 128), dtype=torch.float32, device=dev)
+    act = torch.empty((N, I), dtype=torch.uint8, device=dev)
+    act_s = torch.empty((N, I // 128), dtype=torch.float32, device=dev)
+    y = torch.empty((N, H), dtype=torch.bfloat16, device=dev)
+    out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    bufs = (rx, rs, act, act_s, y)
+    ws = moe.layer_workspace(dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+
+    def four(ev=None):
+        if ev: hev.record(ev[0], stream)
+        moe.dispatch(x, lay.pos, N, "fp8_pow2", rx, rs)
+        if ev: hev.record(ev[1], stream)
+        moe.expert_up(rx, rs, w1, w1s, lay.cnt_e, lay.off_e, 0, act, act_s)
+        if ev: hev.record(ev[2], stream)
+        moe.expert_down(act, act_s, w2, w2s, lay.cnt_e, lay.off_e, 0, y)
+        if ev: hev.record(ev[3], stream)
+        moe.combine(y, lay.pos, w, out)
+        if ev: hev.record(ev[4], stream)
+
+    def one():
+        moe.layer_forward(x, lay.pos, w, lay.cnt_e, lay.off_e, w1, w1s, w2, w2s, N, 0, workspace=ws, out=out,
+                          buffers=bufs)
+
+    def timed(f, K, nev):
+        evs = [hev.create(nev) for _ in range(K)] if nev else None
+        s0, s1 = hev.create(2)
+        if hasattr(torch.cuda, "_sleep"):
+            torch.cuda._sleep(int(2e7))
+        hev.record(s0, stream)
+        for i in range(K):
+            f(evs[i]) if nev else f()
+        hev.record(s1, stream)
+        torch.cuda.synchronize()
+        return hev.ms(s0, s1) / K * 1e3, evs
+
+    for _ in range(args.warmup):
+        four()
+        one()
+    torch.cuda.synchronize()
+    K = args.steps
+    four_us, evs = timed(four, K, 5)
+    st = np.array([[hev.ms(e[q], e[q + 1]) for q in range(4)] for e in evs]) * 1e3
+    four_nev_us, _ = timed(lambda: four(), K, 0)
+    one_us, _ = timed(one, K, 0)
+    flops = 2.0 * N * 3 * I * H
+    words = ws.view(torch.int32).cpu().numpy()
+    ticks = ws.view(torch.int64).cpu().numpy()[384:388].astype(np.float64)  # last call, 100 MHz
+    phase_us = np.diff(ticks) / 100.0
+    res = {
+        "metric": "MoE layer after routing (dispatch + expert up + expert down + combine), us per layer",
+        "value": round(one_us, 1), "unit": "us", "n_gpus": 1, "steps": K, "warmup": args.warmup,
+        "ms_per_step": round(one_us / 1e3, 4), "higher_is_better": False, "scaling": "weak",
+        "vs_baseline": None, "dtype": "fp8 e4m3 GEMMs (fp32 accumulate), bf16 combine",
+        "data": "synthetic bf16 tokens, N(0,1) router logits, FP8 weights with power-of-two block scales",
+        "config": {"workload": f"one rank's layer: T={T} H={H} I={I} E={E} top-{k}", "rows": N,
+                   "parallelism": "single GPU"},
+        "one_launch_us": round(one_us, 1),
+        "four_launches_us": round(four_nev_us, 1),
+        "four_launches_stage_us": {n: round(float(v), 1) for n, v in
+                                   zip(("dispatch", "up", "down", "combine"), st.mean(0))},
+        "layer_tflops_one_launch": round(flops / (one_us * 1e-6) / 1e12, 1),
+        "one_launch_phase_us_block0": {n: round(float(v), 1) for n, v in
+                                       zip(("dispatch", "up", "down"), phase_us)},
+        "barrier_workspace_at_rest": bool(words[0] == 0 and words[2] == 0),
+    }
+    print(json.dumps(res), flush=True)
+
+
 def mlp_main(args, torch, moe, hev, dev):
     """The expert MLP between dispatch and combine on one rank's receive
     buffer: moe_expert_up (first layer, SwiGLU, FP8 requantisation) then
@@ -328,7 +414,7 @@ def mlp_main(args, torch, moe, hev, dev):
     value = (f_up + f_down) / ((up_us + down_us) * 1e-6) / 1e12
     dom = "up" if up_us >= down_us else "down"
     ach = tf_up if dom == "up" else tf_down
-    digest = source_digest("mlp.hip", "moe_device.hpp")
+    digest = source_digest("mlp.hip", "mlp_impl.hpp", "moe_device.hpp")
     res = {
         "metric": "expert MLP TFLOP/s (FP8 up + SwiGLU + FP8 requantisation, FP8 down to bf16)",
         "value": round(value, 1), "unit": "TFLOP/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
@@ -363,6 +449,8 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.stage == "layer":
+        return layer_main(args, torch, moe, HipEvents(), dev)
     if args.stage == "mlp":
         return mlp_main(args, torch, moe, HipEvents(), dev)
     wl = W.get(args.workload)
@@ -465,8 +553,8 @@ def main():
     dc_us = disp_us + comb_us
     value = dc_bytes / (dc_us * 1e-6) / 1e9
 
-    kernels = {"dispatch": (disp_us, b["dispatch"], ("dispatch.hip", "moe_device.hpp")),
-               "combine": (comb_us, b["combine"], ("combine.hip", "moe_device.hpp"))}
+    kernels = {"dispatch": (disp_us, b["dispatch"], ("dispatch.hip", "dispatch_impl.hpp", "moe_device.hpp")),
+               "combine": (comb_us, b["combine"], ("combine.hip", "combine_impl.hpp", "moe_device.hpp"))}
     dom = max(kernels, key=lambda k: kernels[k][0])
     dom_us, dom_bytes, dom_src = kernels[dom]
     achieved = dom_bytes / (dom_us * 1e-6) / 1e9

@@ -85,9 +85,13 @@ def lib() -> ctypes.CDLL:
                                           ctypes.POINTER(DispatchCfg)] + [P] * 13 + [P, S, P])
         L.moe_expert_up.argtypes = [ctypes.POINTER(MlpCfg)] + [P] * 9
         L.moe_expert_down.argtypes = [ctypes.POINTER(MlpCfg)] + [P] * 8
+        L.moe_layer_workspace_bytes.argtypes = []
+        L.moe_layer_workspace_bytes.restype = S
+        L.moe_layer_forward.argtypes = ([ctypes.POINTER(MlpCfg), ctypes.c_int, ctypes.c_int] + [P] * 16 +
+                                        [S, P])
         for f in ("moe_route_topk", "moe_get_layout", "moe_dispatch", "moe_combine", "moe_quantize_e4m3",
                   "moe_dispatch_backward", "moe_combine_backward", "moe_route_dispatch", "moe_expert_up",
-                  "moe_expert_down"):
+                  "moe_expert_down", "moe_layer_forward"):
             getattr(L, f).restype = ctypes.c_int
         L.moe_status_string.argtypes = [ctypes.c_int]
         L.moe_status_string.restype = ctypes.c_char_p
@@ -350,6 +354,73 @@ def expert_down(act, act_scales, w2, w2_scales, cnt_e, off_e, capacity: int = 0,
     _check(lib().moe_expert_down(ctypes.byref(cfg), _ptr(cnt_e), _ptr(off_e), _ptr(act), _ptr(act_scales),
                                  _ptr(w2), _ptr(w2_scales), _ptr(y), _stream(dev)))
     return y
+
+
+def layer_workspace(device):
+    """A zeroed barrier workspace for layer_forward (calls that may overlap on
+    different streams need their own)."""
+    torch = _torch()
+    return torch.zeros(lib().moe_layer_workspace_bytes(), dtype=torch.uint8, device=device)
+
+
+def layer_forward(x, pos, topk_w, cnt_e, off_e, w1, w1_scales, w2, w2_scales, num_recv_rows: int,
+                  capacity: int = 0, workspace=None, out=None, buffers=None):
+    """The MoE layer after routing in one launch: FP8 (power-of-two) dispatch
+    of x bf16 [T,H] by pos int32 [T,k] -> expert up (w1 uint8 [E,2I,H]) ->
+    expert down (w2 uint8 [E,H,I]) -> combine with topk_w fp32 [T,k] ->
+    out bf16 [T,H].  cnt_e/off_e from get_layout.  buffers: optional
+    (recv_x, recv_scales, act, act_scales, y) to write the intermediates
+    into; returns (out, buffers)."""
+    torch = _torch()
+    _need(x, "x", torch.bfloat16)
+    dev = x.device
+    T, H = x.shape
+    _need(pos, "pos", torch.int32, device=dev)
+    k = pos.shape[1] if pos.dim() == 2 else 0
+    _need(pos, "pos", torch.int32, (T, k), dev)
+    _need(topk_w, "topk_w", torch.float32, (T, k), dev)
+    E, I2, H2 = w1.shape
+    I = I2 // 2
+    if H2 != H:
+        raise ValueError("w1 must be [E, 2I, H]")
+    N = num_recv_rows
+    _need(w1, "w1", torch.uint8, device=dev)
+    _need(w1_scales, "w1_scales", torch.float32, (E, I2 // 128, H // 128), dev)
+    _need(w2, "w2", torch.uint8, (E, H, I), dev)
+    _need(w2_scales, "w2_scales", torch.float32, (E, H // 128, I // 128), dev)
+    _need(cnt_e, "cnt_e", torch.int32, (E,), dev)
+    if capacity == 0:
+        _need(off_e, "off_e", torch.int32, (E + 1,), dev)
+    if buffers is None:
+        buffers = (torch.empty((N, H), dtype=torch.uint8, device=dev),
+                   torch.empty((N, H // 128), dtype=torch.float32, device=dev),
+                   torch.empty((N, I), dtype=torch.uint8, device=dev),
+                   torch.empty((N, I // 128), dtype=torch.float32, device=dev),
+                   torch.empty((N, H), dtype=torch.bfloat16, device=dev))
+    rx, rs, act, act_s, y = buffers
+    _need(rx, "recv_x", torch.uint8, (N, H), dev)
+    _need(rs, "recv_scales", torch.float32, (N, H // 128), dev)
+    _need(act, "act", torch.uint8, (N, I), dev)
+    _need(act_s, "act_scales", torch.float32, (N, I // 128), dev)
+    _need(y, "y", torch.bfloat16, (N, H), dev)
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    else:
+        _need(out, "out", torch.bfloat16, (T, H), dev)
+    if workspace is None:
+        key = (dev.type, dev.index)
+        if key not in _layer_ws:
+            _layer_ws[key] = layer_workspace(dev)
+        workspace = _layer_ws[key]
+    cfg = MlpCfg(N, H, I, E, capacity)
+    _check(lib().moe_layer_forward(ctypes.byref(cfg), T, k, _ptr(pos), _ptr(topk_w), _ptr(cnt_e), _ptr(off_e),
+                                   _ptr(x), _ptr(w1), _ptr(w1_scales), _ptr(w2), _ptr(w2_scales), _ptr(rx),
+                                   _ptr(rs), _ptr(act), _ptr(act_s), _ptr(y), _ptr(out), _ptr(workspace),
+                                   workspace.numel(), _stream(dev)))
+    return out, buffers
+
+
+_layer_ws = {}
 
 
 def combine(y, pos, topk_w, out=None, units_per_wave: int = 0):

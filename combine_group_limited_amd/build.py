@@ -27,7 +27,8 @@ LIB = os.path.join(PKG, "libcgl_moe.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 RESOURCES = os.path.join(BUILD_DIR, "kernel_resources.txt")
 
-SOURCES = ["moe_api.hip", "route.hip", "layout.hip", "dispatch.hip", "combine.hip", "backward.hip", "fused.hip", "mlp.hip"]
+SOURCES = ["moe_api.hip", "route.hip", "layout.hip", "dispatch.hip", "combine.hip", "backward.hip", "fused.hip", "mlp.hip",
+           "layer.hip"]
 ARCH = os.environ.get("CGL_OFFLOAD_ARCH", "gfx950")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -11,148 +11,16 @@
 // gathers the U 1 KiB pieces of row pos[t,j] (issued together) and folds them
 // into fp32 accumulators with one fma per element; the result is rounded to
 // bf16 once (v_cvt_pk_bf16_f32, nearest-even) and stored with 16-byte writes.
+#include "combine_impl.hpp"
 #include "moe_device.hpp"
 #include "moe_internal.hpp"
 
 namespace cgl {
 namespace {
 
-constexpr int kUnit = 512;
-#ifndef CGL_COMBINE_THREADS
-#define CGL_COMBINE_THREADS 256
-#endif
-// LDS bytes requested per block only to cap how many blocks share a CU
-// (0 = no cap)
-#ifndef CGL_COMBINE_LDS_CAP
-#define CGL_COMBINE_LDS_CAP 0
-#endif
-constexpr int kCombineThreads = CGL_COMBINE_THREADS;  // waves per block = threads / 64
-
-// cache policy of the y gathers and the output writes (1 = streaming)
-#ifndef CGL_COMBINE_LOAD_NT
-#define CGL_COMBINE_LOAD_NT 1
-#endif
-#ifndef CGL_COMBINE_STORE_NT
-#define CGL_COMBINE_STORE_NT 1
-#endif
-// 1: gather slot j+1 while folding slot j; 0: one slot's gathers at a time
-#ifndef CGL_COMBINE_PIPELINE
-#define CGL_COMBINE_PIPELINE 0
-#endif
-
-struct CombineArgs {
-    const uint16_t* y;
-    const int32_t* pos;
-    const float* w;
-    uint16_t* out;
-    int T, H, k, N;
-    int units, chunks;
-};
-
-// Gathers U 16-byte pieces of one row.  Loads are unconditional (a lane past
-// the end of the row reads the row's last piece instead; its result is never
-// stored), so no branch separates the loads and the compiler can overlap them
-// with the folds of the previous slot.
-template <int U>
-__device__ __forceinline__ void gather_row(u32x4 (&v)[U], const uint16_t* src, int u0, int lane, int H) {
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-        const int c = min((u0 + u) * kUnit + lane * 8, H - 8);
-        v[u] = load_stream<CGL_COMBINE_LOAD_NT>((const u32x4*)(src + c));
-    }
-}
-
-template <int U>
-__device__ __forceinline__ void fold_row(float (&acc)[U][8], const u32x4 (&v)[U], float wj) {
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-        acc[u][0] = __builtin_fmaf(wj, bf16_lo(v[u].x), acc[u][0]);
-        acc[u][1] = __builtin_fmaf(wj, bf16_hi(v[u].x), acc[u][1]);
-        acc[u][2] = __builtin_fmaf(wj, bf16_lo(v[u].y), acc[u][2]);
-        acc[u][3] = __builtin_fmaf(wj, bf16_hi(v[u].y), acc[u][3]);
-        acc[u][4] = __builtin_fmaf(wj, bf16_lo(v[u].z), acc[u][4]);
-        acc[u][5] = __builtin_fmaf(wj, bf16_hi(v[u].z), acc[u][5]);
-        acc[u][6] = __builtin_fmaf(wj, bf16_lo(v[u].w), acc[u][6]);
-        acc[u][7] = __builtin_fmaf(wj, bf16_hi(v[u].w), acc[u][7]);
-    }
-}
-
-__device__ __forceinline__ float lane_float(float v, int j) {
-    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), j));
-}
-
-// The token's k receive rows and weights are read once, one per lane, and
-// broadcast with readlane, so the slot loop issues only the row gathers.
-// When all k rows are valid (always, except for pairs dropped in padded
-// mode) the slot loop is software-pipelined: slot j+1's gathers are in
-// flight while slot j is folded into the accumulators, in slot order.  With k
-// a compile-time constant (KC = 8, 4 or 2) the loop unrolls over two
-// alternating buffers, so the waits count exactly the gathers still needed.
 template <int U, int KC>
 __global__ __launch_bounds__(kCombineThreads) void combine_kernel(CombineArgs a) {
-    const int lane = threadIdx.x & 63;
-    const int wave = blockIdx.x * (kCombineThreads / kWave) + wave_in_block();
-    const int t = wave / a.chunks;
-    if (t >= a.T) return;  // wave-uniform
-    const int u0 = (wave - t * a.chunks) * U;
-    const int k = KC > 0 ? KC : a.k;
-
-    int pv = (lane < k) ? a.pos[(size_t)t * k + lane] : -1;
-    if (pv >= a.N) pv = -1;                     // out of range: contributes nothing
-    // no weights (the backward of dispatch): every slot weighs 1
-    const float wv = (lane < k) ? (a.w ? a.w[(size_t)t * k + lane] : 1.0f) : 0.0f;
-    const uint64_t kmask = (k >= 64) ? ~0ull : ((1ull << k) - 1ull);
-    const bool all_valid = __ballot(lane < k && pv >= 0) == kmask;
-
-    float acc[U][8];
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-#pragma unroll
-        for (int i = 0; i < 8; ++i) acc[u][i] = 0.0f;
-
-    if (CGL_COMBINE_PIPELINE && all_valid && KC > 0) {
-        u32x4 buf[2][U];
-        gather_row<U>(buf[0], a.y + (size_t)__builtin_amdgcn_readlane(pv, 0) * a.H, u0, lane, a.H);
-#pragma unroll
-        for (int j = 0; j < (KC > 0 ? KC : 1); ++j) {
-            if (j + 1 < KC)
-                gather_row<U>(buf[(j + 1) & 1], a.y + (size_t)__builtin_amdgcn_readlane(pv, j + 1) * a.H, u0, lane,
-                              a.H);
-            fold_row<U>(acc, buf[j & 1], lane_float(wv, j));
-        }
-    } else if (CGL_COMBINE_PIPELINE && all_valid) {
-        u32x4 cur[U], nxt[U];
-        gather_row<U>(cur, a.y + (size_t)__builtin_amdgcn_readlane(pv, 0) * a.H, u0, lane, a.H);
-        for (int j = 0; j + 1 < k; ++j) {
-            gather_row<U>(nxt, a.y + (size_t)__builtin_amdgcn_readlane(pv, j + 1) * a.H, u0, lane, a.H);
-            fold_row<U>(acc, cur, lane_float(wv, j));
-#pragma unroll
-            for (int u = 0; u < U; ++u) cur[u] = nxt[u];
-        }
-        fold_row<U>(acc, cur, lane_float(wv, k - 1));
-    } else {
-        for (int j = 0; j < k; ++j) {
-            const int p = __builtin_amdgcn_readlane(pv, j);
-            if (p < 0) continue;  // wave-uniform
-            u32x4 v[U];
-            gather_row<U>(v, a.y + (size_t)p * a.H, u0, lane, a.H);
-            fold_row<U>(acc, v, lane_float(wv, j));
-        }
-    }
-
-    uint16_t* orow = a.out + (size_t)t * a.H;
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-        const int c = (u0 + u) * kUnit + lane * 8;
-        if (c < a.H) {
-            u32x4 o;
-            o.x = pack_bf16x2(acc[u][0], acc[u][1]);
-            o.y = pack_bf16x2(acc[u][2], acc[u][3]);
-            o.z = pack_bf16x2(acc[u][4], acc[u][5]);
-            o.w = pack_bf16x2(acc[u][6], acc[u][7]);
-            store_stream<CGL_COMBINE_STORE_NT>(o, (u32x4*)(orow + c));
-        }
-    }
+    combine_wave<U, KC>(a, blockIdx.x * (kCombineThreads / kWave) + wave_in_block());
 }
 
 template <int U>
@@ -173,7 +41,7 @@ hipError_t launch_u(CombineArgs a, hipStream_t s) {
 }  // namespace
 
 int combine_units_per_wave(int T, int H) {
-    const int units = (H + kUnit - 1) / kUnit;
+    const int units = (H + kCombineUnit - 1) / kCombineUnit;
     static const int choices[] = {7, 4, 2, 1};
     for (int u : choices) {
         if (u > units || units % u) continue;
@@ -193,7 +61,7 @@ hipError_t launch_combine(const uint16_t* y, const int32_t* pos, const float* w,
     a.H = H;
     a.k = k;
     a.N = N;
-    a.units = (H + kUnit - 1) / kUnit;
+    a.units = (H + kCombineUnit - 1) / kCombineUnit;
     if (upw <= 0) upw = combine_units_per_wave(T, H);
     switch (upw) {
         case 7: return launch_u<7>(a, stream);

@@ -15,129 +15,21 @@
 // them once, quantises them once, and writes the codes (8 bytes per lane, a
 // 512-byte contiguous store per unit) and the scales to each of the token's k
 // receive rows.  Every output byte is written by exactly one lane.
+#include "dispatch_impl.hpp"
 #include "moe_device.hpp"
 #include "moe_internal.hpp"
 
 namespace cgl {
 namespace {
 
-constexpr int kUnit = 512;             // channels per wave-wide 16-byte load
-#ifndef CGL_DISPATCH_THREADS
-#define CGL_DISPATCH_THREADS 256
-#endif
-// LDS bytes requested per block only to cap how many blocks share a CU
-// (0 = no cap)
-#ifndef CGL_DISPATCH_LDS_CAP
-#define CGL_DISPATCH_LDS_CAP 0
-#endif
-constexpr int kDispatchThreads = CGL_DISPATCH_THREADS;  // waves per block = threads / 64
-constexpr long long kDrainWaves = 2048;
-
-// cache policy of the x reads and the receive-buffer writes (1 = streaming).
-// Measured on MI355X at 4096 x 7168 top-8: streaming loads with ordinary
-// stores are fastest in the dispatch -> combine sequence.
-#ifndef CGL_DISPATCH_LOAD_NT
-#define CGL_DISPATCH_LOAD_NT 1
-#endif
-#ifndef CGL_DISPATCH_STORE_NT
-#define CGL_DISPATCH_STORE_NT 0
-#endif
-// 1: wait until a destination row's stores have completed before starting
-// the next row (fewer rows open at once across the chip) when the grid has
-// at least kDrainWaves waves; smaller grids leave every row in flight.
-// Measured on MI355X: 48.9 vs 52.6 us at 4096 tokens (4 096 waves), but
-// 4.6 vs 3.8 us at 128 tokens (1 792 waves).
-#ifndef CGL_DISPATCH_DRAIN
-#define CGL_DISPATCH_DRAIN 1
-#endif
-
-struct DispatchArgs {
-    const uint16_t* x;
-    const int32_t* pos;
-    void* recv_x;
-    float* recv_scales;
-    int T, H, k, N, S;
-    int units;   // ceil(H / 512)
-    int chunks;  // ceil(units / U): waves per token
-    int drain;   // wait for each row's stores before the next
-};
-
-__device__ __forceinline__ u32x4 load16(const uint16_t* p) {
-    return load_stream<CGL_DISPATCH_LOAD_NT>((const u32x4*)p);
-}
-
 template <int U, bool POW2>
 __global__ __launch_bounds__(kDispatchThreads) void dispatch_fp8_kernel(DispatchArgs a) {
-    const int lane = threadIdx.x & 63;
-    const int wave = blockIdx.x * (kDispatchThreads / kWave) + wave_in_block();
-    const int t = wave / a.chunks;
-    if (t >= a.T) return;  // wave-uniform
-    const int u0 = (wave - t * a.chunks) * U;
-    const uint16_t* xrow = a.x + (size_t)t * a.H;
-    // the token's k receive rows, one per lane, read once up front so the
-    // store loop below issues no loads (a load there would make the wave wait
-    // for its outstanding stores too)
-    const int pv = (lane < a.k) ? a.pos[(size_t)t * a.k + lane] : -1;
-
-    u32x4 v[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-        const int c = (u0 + u) * kUnit + lane * 8;
-        v[u] = (c < a.H) ? load16(xrow + c) : u32x4{0u, 0u, 0u, 0u};
-    }
-
-    u32x2 code[U];
-    float scale[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-        code[u] = quantize_unit<POW2>(v[u], scale[u]);
-    }
-
-    uint8_t* rx = (uint8_t*)a.recv_x;
-    for (int j = 0; j < a.k; ++j) {
-        const int p = __builtin_amdgcn_readlane(pv, j);
-        if (p < 0 || p >= a.N) continue;  // dropped pair (wave-uniform)
-        uint8_t* dst = rx + (size_t)p * a.H;
-        float* sdst = a.recv_scales + (size_t)p * a.S;
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int c = (u0 + u) * kUnit + lane * 8;
-            if (c < a.H) {
-                store_stream<CGL_DISPATCH_STORE_NT>(code[u], (u32x2*)(dst + c));
-                if ((lane & 15) == 0) sdst[c >> 7] = scale[u];
-            }
-        }
-        if (CGL_DISPATCH_DRAIN && a.drain) __builtin_amdgcn_s_waitcnt(kWaitStores);
-    }
+    dispatch_fp8_wave<U, POW2>(a, blockIdx.x * (kDispatchThreads / kWave) + wave_in_block());
 }
 
 template <int U>
 __global__ __launch_bounds__(kDispatchThreads) void dispatch_bf16_kernel(DispatchArgs a) {
-    const int lane = threadIdx.x & 63;
-    const int wave = blockIdx.x * (kDispatchThreads / kWave) + wave_in_block();
-    const int t = wave / a.chunks;
-    if (t >= a.T) return;
-    const int u0 = (wave - t * a.chunks) * U;
-    const uint16_t* xrow = a.x + (size_t)t * a.H;
-    const int pv = (lane < a.k) ? a.pos[(size_t)t * a.k + lane] : -1;
-    u32x4 v[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-        const int c = (u0 + u) * kUnit + lane * 8;
-        v[u] = (c < a.H) ? load16(xrow + c) : u32x4{0u, 0u, 0u, 0u};
-    }
-    uint16_t* rx = (uint16_t*)a.recv_x;
-    for (int j = 0; j < a.k; ++j) {
-        const int p = __builtin_amdgcn_readlane(pv, j);
-        if (p < 0 || p >= a.N) continue;
-        uint16_t* dst = rx + (size_t)p * a.H;
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int c = (u0 + u) * kUnit + lane * 8;
-            if (c < a.H) store_stream<CGL_DISPATCH_STORE_NT>(v[u], (u32x4*)(dst + c));
-        }
-        if (CGL_DISPATCH_DRAIN && a.drain) __builtin_amdgcn_s_waitcnt(kWaitStores);
-    }
+    dispatch_bf16_wave<U>(a, blockIdx.x * (kDispatchThreads / kWave) + wave_in_block());
 }
 
 template <int U>
@@ -161,7 +53,7 @@ hipError_t launch_u(DispatchArgs a, int dtype, hipStream_t s) {
 }  // namespace
 
 int dispatch_units_per_wave(int T, int H) {
-    const int units = (H + kUnit - 1) / kUnit;
+    const int units = (H + kDispatchUnit - 1) / kDispatchUnit;
     // enough waves to fill 256 CUs several times over, otherwise fewer loads
     // per wave; U must divide the unit count to avoid idle lanes
     static const int choices[] = {14, 8, 7, 4, 2, 1};
@@ -184,7 +76,7 @@ hipError_t launch_dispatch(const uint16_t* x, const int32_t* pos, void* recv_x, 
     a.k = k;
     a.N = N;
     a.S = H / 128;
-    a.units = (H + kUnit - 1) / kUnit;
+    a.units = (H + kDispatchUnit - 1) / kDispatchUnit;
     if (upw <= 0) upw = dispatch_units_per_wave(T, H);
     switch (upw) {
         case 14: return launch_u<14>(a, dtype, stream);

@@ -31,6 +31,7 @@
 // block arrives.  Device-scope release/acquire fences would instead write back
 // and invalidate each XCD's whole L2 once per block: measured on MI355X at
 // 128 tokens, they cost 11 us of a 17 us launch.
+#include "grid_barrier.hpp"
 #include "moe_internal.hpp"
 #include "route_impl.hpp"
 
@@ -41,7 +42,6 @@ constexpr int kFusedThreads = 256;
 constexpr int kFusedWaves = kFusedThreads / kWave;
 constexpr int kUnitChannels = 512;  // one 16-byte load per lane
 constexpr int kSliceRows = 2048;    // recv_src rows per LDS slice
-constexpr int kSpinLimit = 1 << 22;  // barrier polls before a block gives up (seconds)
 
 struct FusedArgs {
     RouteArgs r;  // logits -> idx [T,k], w [T,k]; T, E, G, g, k, n, score_fn, renorm
@@ -90,60 +90,6 @@ __device__ __forceinline__ u32x2 quantize(const FusedArgs& a, const u32x4& v, fl
     return quantize_unit<false>(v, scale);  // also run for BF16, result unused
 }
 
-// Grid-wide barrier, a two-level tree of arrival counters: block b arrives
-// at the counter of group b % 8 (each counter and flag on its own 256-byte
-// line of the workspace), the last block of a group at the top counter, and
-// the last block overall resets the counters and publishes the next
-// generation to every group's flag, which the group's other blocks poll.  So
-// no more than ceil(blocks / 8) atomics queue on one address (a single
-// counter costs 10 us at 448 blocks, the tree 3 us).  Polls are bounded; a
-// block that gives up (only possible if the grid is not resident) counts
-// itself in word 2 and returns false in all its threads.  Counters and flags
-// only order control: the data they guard travels by device-scope atomics.
-constexpr int kGroups = 8;
-constexpr int kGroupStride = 64;  // 32-bit words: 256 bytes per group
-
-__device__ bool grid_barrier(uint32_t* ws) {
-    __shared__ int gave_up;
-    __builtin_amdgcn_s_waitcnt(kWaitStores);  // this wave's stores have completed
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        const int nb = gridDim.x, c = blockIdx.x % kGroups;
-        const int in_group = (nb - c + kGroups - 1) / kGroups;
-        const int groups = nb < kGroups ? nb : kGroups;
-        uint32_t* counter = ws + kGroupStride * (1 + c);
-        uint32_t* flag = counter + 1;
-        const uint32_t gen = __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        bool last = false;
-        if (__hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-            (uint32_t)(in_group - 1)) {
-            __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            if (__hip_atomic_fetch_add(&ws[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-                (uint32_t)(groups - 1)) {
-                __hip_atomic_store(&ws[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                for (int q = 0; q < groups; ++q)
-                    __hip_atomic_store(ws + kGroupStride * (1 + q) + 1, gen + 1u, __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT);
-                last = true;
-            }
-        }
-        int fail = 0;
-        if (!last) {
-            int spins = 0;
-            while (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == gen) {
-                if (++spins > kSpinLimit) {
-                    fail = 1;
-                    __hip_atomic_fetch_add(&ws[2], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    break;
-                }
-                __builtin_amdgcn_s_sleep(2);
-            }
-        }
-        gave_up = fail;
-    }
-    __syncthreads();
-    return gave_up == 0;
-}
 
 template <int EPL, int LPG>
 __global__ __launch_bounds__(kFusedThreads) void fused_decode_kernel(FusedArgs a) {
@@ -169,7 +115,7 @@ __global__ __launch_bounds__(kFusedThreads) void fused_decode_kernel(FusedArgs a
     const u32x2 q0 = quantize(a, v0, s0);
 
     // ---- 2. every token routed ---------------------------------------------
-    if (!grid_barrier(a.bar)) return;  // block-uniform
+    if (!grid_barrier<false>(a.bar)) return;  // block-uniform
 
     // ---- 3. the layout of the whole batch, in LDS ----------------------------
     for (int i = tid; i < a.nch * E; i += kFusedThreads) emask[i] = 0;

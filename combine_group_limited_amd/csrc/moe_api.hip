@@ -373,6 +373,46 @@ moe_status moe_expert_down(const moe_mlp_cfg* c, const int32_t* cnt_e, const int
                       "expert_down launch");
 }
 
+size_t moe_layer_workspace_bytes(void) { return 4096; }
+
+moe_status moe_layer_forward(const moe_mlp_cfg* c, int num_tokens, int topk, const int32_t* pos,
+                             const float* topk_w, const int32_t* cnt_e, const int32_t* off_e, const uint16_t* x,
+                             const uint8_t* w1, const float* w1_scales, const uint8_t* w2, const float* w2_scales,
+                             uint8_t* recv_x, float* recv_scales, uint8_t* act, float* act_scales, uint16_t* y,
+                             uint16_t* out, void* workspace, size_t workspace_bytes, void* stream) {
+    const moe_status st = check_mlp_cfg(c, "layer_forward");
+    if (st != MOE_OK) return st;
+    const int T = num_tokens, k = topk, N = c->num_rows, H = c->hidden, I = c->inter, E = c->num_experts;
+    if (T < 0) return fail(MOE_ERR_INVALID, "layer_forward: num_tokens %d < 0", T);
+    if (k < 1 || k > 64) return fail(MOE_ERR_INVALID, "layer_forward: topk %d outside [1, 64]", k);
+    if (H > 8192) return fail(MOE_ERR_INVALID, "layer_forward: hidden %d above 8192", H);
+    if ((int64_t)N * H > (1ll << 32) || (int64_t)N * I > (1ll << 32))
+        return fail(MOE_ERR_UNSUPPORTED, "layer_forward: num_rows*hidden or num_rows*inter above 2^32");
+    if ((int64_t)T * H >= (1ll << 40) || (int64_t)T * k >= (1ll << 31))
+        return fail(MOE_ERR_INVALID, "layer_forward: num_tokens too large");
+    if (T == 0 || N == 0) return ok();
+    if (!pos || !topk_w || !cnt_e || (c->capacity == 0 && !off_e) || !x || !w1 || !w1_scales || !w2 ||
+        !w2_scales || !recv_x || !recv_scales || !act || !act_scales || !y || !out)
+        return fail(MOE_ERR_INVALID, "layer_forward: NULL array");
+    if (!aligned(x, 16) || !aligned(w1, 16) || !aligned(w2, 16) || !aligned(recv_x, 16) || !aligned(act, 16) ||
+        !aligned(y, 16) || !aligned(out, 16) || !aligned(pos, 4) || !aligned(topk_w, 4) || !aligned(cnt_e, 4) ||
+        !aligned(off_e, 4) || !aligned(w1_scales, 4) || !aligned(w2_scales, 4) || !aligned(recv_scales, 4) ||
+        !aligned(act_scales, 4))
+        return fail(MOE_ERR_INVALID, "layer_forward: code and row arrays must be 16-byte aligned, the others 4-byte");
+    if (!workspace || workspace_bytes < moe_layer_workspace_bytes() || !aligned(workspace, 16))
+        return fail(MOE_ERR_WORKSPACE, "layer_forward: workspace must be %zu bytes, 16-byte aligned (got %zu)",
+                    moe_layer_workspace_bytes(), workspace ? workspace_bytes : (size_t)0);
+    int supported = 0;
+    const size_t lds = layer_lds_bytes(N, H, I, E, &supported);
+    if (!supported || lds > 160 * 1024)
+        return fail(MOE_ERR_UNSUPPORTED,
+                    "layer_forward: no one-launch kernel for this tile configuration (use the four calls)");
+    return hip_status(launch_layer(x, pos, topk_w, cnt_e, off_e, w1, w1_scales, w2, w2_scales, recv_x, recv_scales,
+                                   act, act_scales, y, out, (uint32_t*)workspace, T, k, N, H, I, E, c->capacity,
+                                   (hipStream_t)stream),
+                      "layer_forward launch");
+}
+
 moe_status moe_quantize_e4m3(const float* in, uint8_t* out, int64_t n, void* stream) {
     if (n < 0) return fail(MOE_ERR_INVALID, "quantize: n < 0");
     if (n == 0) return ok();

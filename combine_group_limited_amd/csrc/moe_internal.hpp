@@ -40,6 +40,14 @@ hipError_t launch_fused_decode(const float* logits, const uint16_t* x, int32_t* 
                                int G, int g, int k, int n, int score_fn, int renorm, int R, int C, int A, int N,
                                int H, int dtype, hipStream_t stream);
 
+// The MoE layer after routing in one launch (dispatch -> up -> down -> combine).
+size_t layer_lds_bytes(int N, int H, int I, int E, int* supported);
+hipError_t launch_layer(const uint16_t* x, const int32_t* pos, const float* topk_w, const int32_t* cnt_e,
+                        const int32_t* off_e, const uint8_t* w1, const float* w1s, const uint8_t* w2,
+                        const float* w2s, uint8_t* recv_x, float* recv_s, uint8_t* act, float* act_s, uint16_t* y,
+                        uint16_t* out, uint32_t* barrier, int T, int k, int N, int H, int I, int E, int C,
+                        hipStream_t stream);
+
 // Expert MLP (grouped FP8 GEMMs with power-of-two block scales).
 size_t expert_mlp_lds_bytes(int N, int K, int E);
 hipError_t prepare_expert_mlp(bool up, int N, int K, int E);

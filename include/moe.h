@@ -361,6 +361,54 @@ moe_status moe_expert_down(const moe_mlp_cfg* cfg, const int32_t* cnt_e, const i
                            const float* w2_scales, uint16_t* y, void* stream);
 
 /* ------------------------------------------------------------------------ */
+/* moe_layer_forward -- the MoE layer after routing in ONE kernel launch:    */
+/* dispatch -> expert up -> expert down -> combine.                         */
+/*                                                                          */
+/* Follows the Mega MoE news page (dispatch, the first linear layer,        */
+/* SwiGLU, the second linear layer and combine fused into one kernel).      */
+/* Computes exactly, bit for bit, what this sequence computes and writes    */
+/* every array it writes:                                                   */
+/*   moe_dispatch(MOE_DISPATCH_FP8_E4M3_POW2; x, pos -> recv_x, recv_scales)*/
+/*   moe_expert_up(cfg; recv_x, recv_scales, w1, w1_scales -> act,          */
+/*                 act_scales)                                              */
+/*   moe_expert_down(cfg; act, act_scales, w2, w2_scales -> y)              */
+/*   moe_combine(y, pos, topk_w -> out)                                     */
+/* with num_tokens T and topk k for dispatch and combine, num_recv_rows =   */
+/* cfg->num_rows, hidden = cfg->hidden.  The blocks of the launch meet at   */
+/* three grid-wide barriers; one block per compute unit, all resident.      */
+/*                                                                          */
+/* x bf16 [T,H], pos int32 [T,k], topk_w fp32 [T,k], cnt_e and off_e as for */
+/* the expert MLP, w1/w1_scales/w2/w2_scales as for the expert MLP in;      */
+/* recv_x uint8 [N,H], recv_scales fp32 [N,H/128], act uint8 [N,I],         */
+/* act_scales fp32 [N,I/128], y bf16 [N,H] (the intermediate arrays, all    */
+/* written), out bf16 [T,H] out.  All caller-allocated.                    */
+/* workspace: at least moe_layer_workspace_bytes() of device memory,        */
+/* 16-byte aligned, ZEROED BEFORE ITS FIRST USE; the barriers leave it at   */
+/* rest after every call.  Calls that may run at the same time need         */
+/* different workspaces.  Its third 32-bit word counts blocks that stopped  */
+/* waiting at a barrier after about a second (only if the GPU cannot hold   */
+/* the whole grid, e.g. while other kernels occupy it); it stays 0 in       */
+/* normal use, and the outputs of a call that raised it are incomplete.    */
+/* Words 768..775 receive, as four 64-bit values (low word first), the     */
+/* GPU's constant 100-MHz clock (s_memrealtime) read by block 0 at the      */
+/* start and after each barrier: phase timings, for diagnostics only.       */
+/* Limits: those of moe_dispatch, moe_expert_up, moe_expert_down and        */
+/* moe_combine, 1 <= k <= 64; and a tile configuration with a one-launch    */
+/* kernel (256-row tiles, or 128-row tiles with three stage buffers for     */
+/* both H and I; true for H and I up to 16384): MOE_ERR_UNSUPPORTED         */
+/* otherwise (use the four calls).  Arrays of codes and bf16 rows 16-byte   */
+/* aligned, the others 4-byte.                                              */
+/* ------------------------------------------------------------------------ */
+size_t moe_layer_workspace_bytes(void);
+
+moe_status moe_layer_forward(const moe_mlp_cfg* cfg, int num_tokens, int topk, const int32_t* pos,
+                             const float* topk_w, const int32_t* cnt_e, const int32_t* off_e,
+                             const uint16_t* x, const uint8_t* w1, const float* w1_scales,
+                             const uint8_t* w2, const float* w2_scales, uint8_t* recv_x,
+                             float* recv_scales, uint8_t* act, float* act_scales, uint16_t* y,
+                             uint16_t* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
 /* moe_quantize_e4m3 -- the element conversion moe_dispatch uses, exposed   */
 /* on its own: out[i] = E4M3FN nearest-even of in[i], magnitudes above 448  */
 /* saturate to 448, sign kept (codes for NaN inputs are unspecified).       */

@@ -1,0 +1,103 @@
+"""The MoE layer after routing in one launch (moe_layer_forward): dispatch
+(FP8, power-of-two scales) -> expert up -> expert down -> combine in a
+persistent grid with grid-wide barriers.  Every array it writes (receive
+codes and scales, act codes and scales, expert outputs y, combined output)
+must equal, bit for bit, what the four separate calls write on the same
+inputs: compact, tile-aligned and padded layouts, 256-row and 128-row expert
+tiles, and several calls in a row on one barrier workspace, which must be
+left at rest."""
+import sys
+
+import numpy as np
+import pytest
+
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import combine_group_limited_amd as moe  # noqa: E402
+
+DEV = torch.device("cuda:0")
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def bf16_to_dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(DEV).view(torch.bfloat16)
+
+
+def bits(t):
+    return t.contiguous().view(torch.uint8).cpu().numpy()
+
+
+def fresh(N, H, I):
+    return (torch.full((N, H), 0x11, dtype=torch.uint8, device=DEV),
+            torch.full((N, H // 128), 3.0, dtype=torch.float32, device=DEV),
+            torch.full((N, I), 0x22, dtype=torch.uint8, device=DEV),
+            torch.full((N, I // 128), 5.0, dtype=torch.float32, device=DEV),
+            torch.full((N, H), 77, dtype=torch.int16, device=DEV).view(torch.bfloat16))
+
+
+@pytest.mark.parametrize("T,H,I,E,G,g,k,R,A,C", [
+    (256, 512, 256, 16, 4, 2, 4, 4, 128, 0),      # aligned regions, 128-row tiles
+    (300, 1024, 384, 32, 8, 4, 8, 8, 0, 0),       # compact, ragged tails
+    (128, 7168, 128, 256, 8, 4, 8, 32, 128, 0),   # decode-sized, 256 experts
+    (2048, 1024, 512, 8, 4, 2, 2, 8, 0, 0),       # 256-row tiles
+    (512, 1024, 256, 16, 4, 2, 4, 4, 0, 160),     # padded (capacity) layout, drops
+])
+def test_layer_one_launch_matches_four_calls(T, H, I, E, G, g, k, R, A, C):
+    say(f"[gpu] one-launch layer T={T} H={H} I={I} E={E} k={k} align={A} capacity={C}")
+    wl = W.custom("layer1", T=T, H=H, E=E, G=G, g=g, k=k, score="sigmoid", R=R, dtype="fp8")
+    mw = W.MlpWorkload("layer1_mlp", N=1, H=H, I=I, E=E, seed=7)
+    w1, w1s = W.gen_mlp_weights(mw, "w1")
+    w2, w2s = W.gen_mlp_weights(mw, "w2")
+    d = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+    w1, w1s, w2, w2s = d(w1), d(w1s), d(w2), d(w2s)
+    ws = moe.layer_workspace(DEV)
+    for rep, seed in enumerate([0, 1, 2]):
+        wl2 = wl.replace(seed=seed)
+        x = bf16_to_dev(W.gen_x(wl2))
+        idx, w = moe.route_topk(d(W.gen_logits(wl2)), G, g, k)
+        lay = moe.get_layout(idx, E, R, C, align_rows=A)
+        N = lay.num_recv_rows
+        # the four calls
+        rx, rs, act, act_s, y = fresh(N, H, I)
+        moe.dispatch(x, lay.pos, N, "fp8_pow2", rx, rs)
+        moe.expert_up(rx, rs, w1, w1s, lay.cnt_e, lay.off_e, C, act, act_s)
+        moe.expert_down(act, act_s, w2, w2s, lay.cnt_e, lay.off_e, C, y)
+        out = moe.combine(y, lay.pos, w)
+        # one launch
+        bufs = fresh(N, H, I)
+        out1, _ = moe.layer_forward(x, lay.pos, w, lay.cnt_e, lay.off_e, w1, w1s, w2, w2s, N, C,
+                                    workspace=ws, buffers=bufs)
+        torch.cuda.synchronize()
+        for name, a, b in zip(("recv_x", "recv_scales", "act", "act_scales", "y"), (rx, rs, act, act_s, y), bufs):
+            assert np.array_equal(bits(a), bits(b)), (rep, name)
+        assert np.array_equal(bits(out), bits(out1)), (rep, "out")
+        words = ws.view(torch.int32).cpu().numpy()
+        assert words[0] == 0 and words[2] == 0, words[:3]
+        say(f"   call {rep} (seed {seed}): every array identical to the four calls")
+
+
+def test_layer_rejects_small_workspace():
+    """A workspace below moe_layer_workspace_bytes() is reported, not used."""
+    T, H, I, E, k = 64, 512, 256, 4, 2
+    x = torch.zeros((T, H), dtype=torch.bfloat16, device=DEV)
+    pos = torch.zeros((T, k), dtype=torch.int32, device=DEV)
+    w = torch.zeros((T, k), dtype=torch.float32, device=DEV)
+    cnt = torch.zeros((E,), dtype=torch.int32, device=DEV)
+    off = torch.zeros((E + 1,), dtype=torch.int32, device=DEV)
+    w1 = torch.zeros((E, 2 * I, H), dtype=torch.uint8, device=DEV)
+    w1s = torch.ones((E, 2 * I // 128, H // 128), dtype=torch.float32, device=DEV)
+    w2 = torch.zeros((E, H, I), dtype=torch.uint8, device=DEV)
+    w2s = torch.ones((E, H // 128, I // 128), dtype=torch.float32, device=DEV)
+    small = torch.zeros(16, dtype=torch.uint8, device=DEV)
+    with pytest.raises(moe.MoeError, match="workspace"):
+        moe.layer_forward(x, pos, w, cnt, off, w1, w1s, w2, w2s, T * k, workspace=small)
