@@ -219,3 +219,33 @@ def test_expert_mlp_32bit_offsets(fn, n_args, vals):
     refused before any array is looked at."""
     assert _mlp(fn, vals, n_args) == moe.MOE_ERR_UNSUPPORTED
     assert moe.lib().moe_last_error()
+
+
+def _layer(cfg_vals, T, k, ws_bytes=4096, ws=None):
+    L = moe.lib()
+    cfg = moe.MlpCfg(*cfg_vals)
+    return L.moe_layer_forward(ctypes.byref(cfg), T, k, *([None] * 15), ws, ws_bytes, None)
+
+
+def test_layer_workspace_size():
+    assert moe.lib().moe_layer_workspace_bytes() == 4096
+
+
+@pytest.mark.parametrize("cfg,T,k,status", [
+    ((100, 7000, 2048, 8, 0), 50, 2, moe.MOE_ERR_INVALID),       # hidden not a multiple of 128
+    ((100, 7168, 2048, 0, 0), 50, 2, moe.MOE_ERR_INVALID),       # no experts
+    ((100, 7168, 2048, 8, 0), -1, 2, moe.MOE_ERR_INVALID),       # negative tokens
+    ((100, 7168, 2048, 8, 0), 50, 0, moe.MOE_ERR_INVALID),       # topk 0
+    ((100, 7168, 2048, 8, 0), 50, 65, moe.MOE_ERR_INVALID),      # topk above 64
+    ((100, 16384, 2048, 8, 0), 50, 2, moe.MOE_ERR_INVALID),      # hidden above 8192
+    ((600000, 8192, 2048, 8, 0), 50, 2, moe.MOE_ERR_UNSUPPORTED),  # N*H above 2^32
+    ((100, 7168, 2048, 8, 0), 50, 2, moe.MOE_ERR_INVALID),       # valid shape, NULL arrays
+])
+def test_layer_rejects(cfg, T, k, status):
+    assert _layer(cfg, T, k) == status
+    assert moe.lib().moe_last_error()
+
+
+def test_layer_zero_tokens_or_rows_is_noop():
+    assert _layer((100, 7168, 2048, 8, 0), 0, 2) == moe.MOE_OK
+    assert _layer((0, 7168, 2048, 8, 0), 50, 2) == moe.MOE_OK
