@@ -55,15 +55,17 @@ __device__ __forceinline__ void layer_dispatch(const DispatchArgs& a, int w0, in
             v[u] = (c < a.H) ? load16(xrow + c) : u32x4{0u, 0u, 0u, 0u};
         }
     };
-    u32x4 v[U];
-    int pv;
+    // two items ahead: v (item w), n1 (w + stride), n2 loaded for w + 2 stride
+    // (past the end, loads re-read the last item: they stay unconditional)
+    auto clampi = [&](int w) { return w < items ? w : items - 1; };
+    u32x4 v[U], n1[U];
+    int pv, p1;
     load_item(w0, v, pv);
+    load_item(clampi(w0 + stride), n1, p1);
     for (int w = w0; w < items; w += stride) {
-        // the next item (the last one re-reads itself: loads stay unconditional)
-        const int wn = w + stride < items ? w + stride : w;
-        u32x4 nv[U];
-        int npv;
-        load_item(wn, nv, npv);
+        u32x4 n2[U];
+        int p2;
+        load_item(clampi(w + 2 * stride), n2, p2);
         const int t = w / a.chunks, u0 = (w - t * a.chunks) * U;
         u32x2 code[U];
         float scale[U];
@@ -85,8 +87,12 @@ __device__ __forceinline__ void layer_dispatch(const DispatchArgs& a, int w0, in
             }
         }
 #pragma unroll
-        for (int u = 0; u < U; ++u) v[u] = nv[u];
-        pv = npv;
+        for (int u = 0; u < U; ++u) {
+            v[u] = n1[u];
+            n1[u] = n2[u];
+        }
+        pv = p1;
+        p1 = p2;
     }
 }
 
