@@ -52,6 +52,7 @@ def fresh(N, H, I):
     (2048, 1024, 512, 8, 4, 2, 2, 8, 0, 0),       # 256-row tiles
     (512, 1024, 256, 16, 4, 2, 4, 4, 0, 160),     # padded (capacity) layout, drops
     (16384, 7168, 2048, 8, 1, 1, 2, 8, 0, 0),     # one rank's layer, the benchmark's shape
+    (200, 640, 256, 8, 2, 1, 3, 4, 0, 0),         # H not a multiple of 512: a partial unit
 ])
 def test_layer_one_launch_matches_four_calls(T, H, I, E, G, g, k, R, A, C):
     say(f"[gpu] one-launch layer T={T} H={H} I={I} E={E} k={k} align={A} capacity={C}")
@@ -102,3 +103,54 @@ def test_layer_rejects_small_workspace():
     small = torch.zeros(16, dtype=torch.uint8, device=DEV)
     with pytest.raises(moe.MoeError, match="workspace"):
         moe.layer_forward(x, pos, w, cnt, off, w1, w1s, w2, w2s, T * k, workspace=small)
+
+
+def test_layer_graph_replays():
+    """moe_layer_forward captured once in a HIP graph and replayed with new
+    tokens and routing weights copied into the captured buffers: every replay
+    equals an eager call on the same inputs (nothing in the launch allocates,
+    synchronises or records a memset node, and the barrier workspace resets
+    itself)."""
+    T, H, I, E, G, g, k, R = 512, 1024, 256, 16, 4, 2, 4, 4
+    wl = W.custom("layer_graph", T=T, H=H, E=E, G=G, g=g, k=k, score="sigmoid", R=R, dtype="fp8")
+    mw = W.MlpWorkload("layer_graph_mlp", N=1, H=H, I=I, E=E, seed=7)
+    d = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+    w1, w1s = map(d, W.gen_mlp_weights(mw, "w1"))
+    w2, w2s = map(d, W.gen_mlp_weights(mw, "w2"))
+    x_s = bf16_to_dev(W.gen_x(wl))
+    idx, w_s = moe.route_topk(d(W.gen_logits(wl)), G, g, k)
+    lay = moe.get_layout(idx, E, R)
+    N = lay.num_recv_rows
+    bufs = fresh(N, H, I)
+    out = torch.empty((T, H), dtype=torch.bfloat16, device=DEV)
+    ws = moe.layer_workspace(DEV)
+
+    def step():
+        moe.layer_forward(x_s, lay.pos, w_s, lay.cnt_e, lay.off_e, w1, w1s, w2, w2s, N, 0, workspace=ws,
+                          out=out, buffers=bufs)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    for rep, seed in enumerate([5, 6, 7]):
+        wl2 = wl.replace(seed=seed)
+        x_s.copy_(bf16_to_dev(W.gen_x(wl2)))
+        w_s.copy_(torch.rand((T, k), dtype=torch.float32, device=DEV))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        ref, rbufs = moe.layer_forward(x_s, lay.pos, w_s, lay.cnt_e, lay.off_e, w1, w1s, w2, w2s, N, 0,
+                                       buffers=fresh(N, H, I))
+        torch.cuda.synchronize()
+        assert same(out, ref), rep
+        assert same(bufs[4], rbufs[4]), rep
+        words = ws.view(torch.int32).cpu().numpy()
+        assert words[0] == 0 and words[2] == 0, words[:3]
+        say(f"   replay {rep} (seed {seed}) identical to an eager call")
