@@ -418,6 +418,8 @@ moe_status moe_quantize_e4m3(const float* in, uint8_t* out, int64_t n, void* str
 
 const char* moe_status_string(moe_status status);
 const char* moe_last_error(void);
+/* moe_abi_version: 5 (adds moe_layer_forward and moe_layer_workspace_bytes */
+/* to version 4; nothing earlier changed).                                  */
 int32_t moe_abi_version(void);
 
 #ifdef __cplusplus

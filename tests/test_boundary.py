@@ -37,7 +37,7 @@ def test_no_undefined_symbols_beyond_runtime():
 
 def test_status_strings_and_version():
     L = moe.lib()
-    assert L.moe_abi_version() == 4
+    assert L.moe_abi_version() == 5
     for s in (0, 1, 2, 4, 5):
         assert L.moe_status_string(s)
 
