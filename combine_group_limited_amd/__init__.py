@@ -370,7 +370,10 @@ def layer_forward(x, pos, topk_w, cnt_e, off_e, w1, w1_scales, w2, w2_scales, nu
     expert down (w2 uint8 [E,H,I]) -> combine with topk_w fp32 [T,k] ->
     out bf16 [T,H].  cnt_e/off_e from get_layout.  buffers: optional
     (recv_x, recv_scales, act, act_scales, y) to write the intermediates
-    into; returns (out, buffers)."""
+    into; returns (out, buffers).  workspace: the barrier workspace; by
+    default one zeroed workspace per device is cached and shared, so calls
+    that may run at the same time on different streams must each pass their
+    own (layer_workspace)."""
     torch = _torch()
     _need(x, "x", torch.bfloat16)
     dev = x.device
