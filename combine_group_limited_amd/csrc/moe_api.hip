@@ -388,7 +388,9 @@ moe_status moe_layer_forward(const moe_mlp_cfg* c, int num_tokens, int topk, con
     if (H > 8192) return fail(MOE_ERR_INVALID, "layer_forward: hidden %d above 8192", H);
     if ((int64_t)N * H > (1ll << 32) || (int64_t)N * I > (1ll << 32))
         return fail(MOE_ERR_UNSUPPORTED, "layer_forward: num_rows*hidden or num_rows*inter above 2^32");
-    if ((int64_t)T * H >= (1ll << 40) || (int64_t)T * k >= (1ll << 31))
+    // T*k, and T times the 512-channel units of a row (the item index of the
+    // dispatch and combine phases, plus two grid strides), fit 32 bits
+    if ((int64_t)T * H >= (1ll << 40) || (int64_t)T * k >= (1ll << 31) || (int64_t)T * ((H + 511) / 512) >= (1ll << 30))
         return fail(MOE_ERR_INVALID, "layer_forward: num_tokens too large");
     if (T == 0 || N == 0) return ok();
     if (!pos || !topk_w || !cnt_e || (c->capacity == 0 && !off_e) || !x || !w1 || !w1_scales || !w2 ||

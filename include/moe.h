@@ -393,11 +393,12 @@ moe_status moe_expert_down(const moe_mlp_cfg* cfg, const int32_t* cnt_e, const i
 /* GPU's constant 100-MHz clock (s_memrealtime) read by block 0 at the      */
 /* start and after each barrier: phase timings, for diagnostics only.       */
 /* Limits: those of moe_dispatch, moe_expert_up, moe_expert_down and        */
-/* moe_combine, 1 <= k <= 64; and a tile configuration with a one-launch    */
-/* kernel (256-row tiles, or 128-row tiles with three stage buffers for     */
-/* both H and I; true for H and I up to 16384): MOE_ERR_UNSUPPORTED         */
-/* otherwise (use the four calls).  Arrays of codes and bf16 rows 16-byte   */
-/* aligned, the others 4-byte.                                              */
+/* moe_combine, 1 <= k <= 64 and T * ceil(H / 512) < 2^30 (MOE_ERR_INVALID  */
+/* otherwise); a tile configuration with a one-launch kernel (256-row       */
+/* tiles, or 128-row tiles with three stage buffers for both H and I, which */
+/* every shape within these limits has), MOE_ERR_UNSUPPORTED otherwise (use */
+/* the four calls).  Arrays of codes and bf16 rows 16-byte aligned, the     */
+/* others 4-byte.                                                           */
 /* ------------------------------------------------------------------------ */
 size_t moe_layer_workspace_bytes(void);
 

@@ -240,6 +240,7 @@ def test_layer_workspace_size():
     ((100, 16384, 2048, 8, 0), 50, 2, moe.MOE_ERR_INVALID),      # hidden above 8192
     ((600000, 8192, 2048, 8, 0), 50, 2, moe.MOE_ERR_UNSUPPORTED),  # N*H above 2^32
     ((100, 7168, 2048, 8, 0), 50, 2, moe.MOE_ERR_INVALID),       # valid shape, NULL arrays
+    ((100, 7168, 2048, 8, 0), 1 << 27, 2, moe.MOE_ERR_INVALID),  # item indices beyond 32 bits
 ])
 def test_layer_rejects(cfg, T, k, status):
     assert _layer(cfg, T, k) == status
