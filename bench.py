@@ -50,6 +50,8 @@ def parse():
     ap.add_argument("--cpu-reps", type=int, default=0, help="oracle repetitions (0: about 10 s)")
     ap.add_argument("--direction", choices=["forward", "backward"], default="forward",
                     help="backward: time combine_backward -> dispatch_backward instead")
+    ap.add_argument("--layer-tokens", type=int, default=16384,
+                    help="tokens of the --stage layer workload (512 gives a decode-sized batch)")
     ap.add_argument("--stage", choices=["dispatch_combine", "mlp", "layer"], default="dispatch_combine",
                     help="mlp: time the expert MLP (up + SwiGLU + FP8 requantisation, down) instead")
     ap.add_argument("--mlp-workload", default="mlp_rank", choices=sorted(W.MLP_WORKLOADS))
@@ -279,11 +281,12 @@ def mlp_cpu_baseline(wl, x, xs, w1, w1s, w2, w2s, start, count, rows: int = 4):
 
 
 def layer_main(args, torch, moe, hev, dev):
-    """The MoE layer after routing on one rank's shape (16384 tokens x 7168,
-    top-2 of 8 experts, I 2048; 32768 receive rows): moe_layer_forward (one
-    launch) against the four calls moe_dispatch -> moe_expert_up ->
-    moe_expert_down -> moe_combine on the same inputs."""
-    T, H, I, E, k = 16384, 7168, 2048, 8, 2
+    """The MoE layer after routing on one rank's shape (--layer-tokens tokens,
+    16384 by default, x 7168, top-2 of 8 experts, I 2048; 2 receive rows per
+    token): moe_layer_forward (one launch) against the four calls
+    moe_dispatch -> moe_expert_up -> moe_expert_down -> moe_combine on the
+    same inputs."""
+    T, H, I, E, k = args.layer_tokens, 7168, 2048, 8, 2
     wl = W.custom("layer_rank", T=T, H=H, E=E, G=1, g=1, k=k, score="sigmoid", R=E, dtype="fp8")
     mw = W.MlpWorkload("layer_rank_mlp", N=1, H=H, I=I, E=E, seed=7)
     d = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)

@@ -19,20 +19,24 @@ constexpr int kSpinLimit = 1 << 22;  // barrier polls before a block gives up (s
 // block that gives up (only possible if the grid is not resident) counts
 // itself in word 2 and returns false in all its threads.  Counters and flags
 // only order control: with FENCE = false the data they guard must travel by
-// device-scope atomics; with FENCE = true every wave releases its ordinary
-// stores at agent scope before its block arrives (write-back of its XCD's
-// L2) and acquires after the barrier (invalidation), so plain loads after
-// the barrier see plain stores made before it by blocks on any XCD.
+// device-scope atomics; with FENCE = true the block's ordinary stores are
+// released at agent scope before it arrives and acquired after the barrier,
+// so plain loads after the barrier see plain stores made before it by blocks
+// on any XCD.  One wave does both for its block: once every wave has waited
+// for its own stores and the block has met, those stores sit in the XCD's L2,
+// which the release writes back whole; the acquire invalidates the CU's L1
+// and the L2 before the block meets again.  (A release and an acquire in
+// every wave cost four whole-L2 write-backs and invalidations per block.)
 constexpr int kGroups = 8;
 constexpr int kGroupStride = 64;  // 32-bit words: 256 bytes per group
 
 template <bool FENCE>
 __device__ bool grid_barrier(uint32_t* ws) {
     __shared__ int gave_up;
-    if (FENCE) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    else __builtin_amdgcn_s_waitcnt(kWaitStores);  // this wave's stores have completed
+    __builtin_amdgcn_s_waitcnt(kWaitStores);  // this wave's stores have completed
     __syncthreads();
     if (threadIdx.x == 0) {
+        if (FENCE) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
         const int nb = gridDim.x, c = blockIdx.x % kGroups;
         const int in_group = (nb - c + kGroups - 1) / kGroups;
         const int groups = nb < kGroups ? nb : kGroups;
@@ -64,10 +68,10 @@ __device__ bool grid_barrier(uint32_t* ws) {
                 __builtin_amdgcn_s_sleep(2);
             }
         }
+        if (FENCE) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
         gave_up = fail;
     }
     __syncthreads();
-    if (FENCE) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     return gave_up == 0;
 }
 
