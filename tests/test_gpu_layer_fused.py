@@ -53,6 +53,11 @@ def fresh(N, H, I):
     (512, 1024, 256, 16, 4, 2, 4, 4, 0, 160),     # padded (capacity) layout, drops
     (16384, 7168, 2048, 8, 1, 1, 2, 8, 0, 0),     # one rank's layer, the benchmark's shape
     (200, 640, 256, 8, 2, 1, 3, 4, 0, 0),         # H not a multiple of 512: a partial unit
+    # more items per wave than one routing batch of the combine phase (64 / k
+    # items) on a 1024-wave grid: two batches at k = 8; at k = 2 a partial
+    # second batch and an odd item count per wave
+    (16384, 512, 128, 16, 4, 2, 8, 4, 0, 0),
+    (40000, 512, 128, 8, 4, 2, 2, 8, 0, 0),
 ])
 def test_layer_one_launch_matches_four_calls(T, H, I, E, G, g, k, R, A, C):
     say(f"[gpu] one-launch layer T={T} H={H} I={I} E={E} k={k} align={A} capacity={C}")
