@@ -24,9 +24,10 @@ constexpr int kSpinLimit = 1 << 22;  // barrier polls before a block gives up (s
 // so plain loads after the barrier see plain stores made before it by blocks
 // on any XCD.  One wave does both for its block: once every wave has waited
 // for its own stores and the block has met, those stores sit in the XCD's L2,
-// which the release writes back whole; the acquire invalidates the CU's L1
-// and the L2 before the block meets again.  (A release and an acquire in
-// every wave cost four whole-L2 write-backs and invalidations per block.)
+// which the release writes back whole; after the barrier the same wave's
+// acquire invalidates the CU's L1 and the XCD's L2, and only then does the
+// closing block barrier let the other waves load.  (A release and an acquire
+// in every wave cost four whole-L2 write-backs and invalidations per block.)
 constexpr int kGroups = 8;
 constexpr int kGroupStride = 64;  // 32-bit words: 256 bytes per group
 

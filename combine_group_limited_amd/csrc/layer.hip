@@ -15,9 +15,10 @@
 // run the standalone arithmetic (quantize_unit, the slot-ordered fma folds,
 // one bf16 rounding) in loops pipelined for a grid of four waves per CU.  So
 // every output is bit for bit what moe_dispatch -> moe_expert_up ->
-// moe_expert_down -> moe_combine write.  The phases hand their results to blocks on other XCDs through
-// ordinary stores, so the barriers release and acquire at agent scope (an L2
-// write-back and invalidation per wave), as a kernel boundary would.
+// moe_expert_down -> moe_combine write.  The phases hand their results to
+// blocks on other XCDs through ordinary stores, so the barriers release and
+// acquire at agent scope (one L2 write-back and one L1/L2 invalidation per
+// block), as a kernel boundary would.
 #include "combine_impl.hpp"
 #include "dispatch_impl.hpp"
 #include "grid_barrier.hpp"
