@@ -57,7 +57,11 @@ def parse():
     ap.add_argument("--mlp-workload", default="mlp_rank", choices=sorted(W.MLP_WORKLOADS))
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also time a plain 1 GiB device copy (reference for counters and peak)")
-    return ap.parse_args()
+    args = ap.parse_args()
+    # 2 receive rows per token x 7168 bytes must stay within the expert MLP's 32-bit row offsets
+    if not 1 <= args.layer_tokens <= 262144:
+        ap.error(f"--layer-tokens must be in [1, 262144], got {args.layer_tokens}")
+    return args
 
 
 class HipEvents:
