@@ -74,6 +74,7 @@ def lib() -> ctypes.CDLL:
         L.moe_layout_workspace_bytes.argtypes = [ctypes.POINTER(LayoutCfg)]
         L.moe_layout_workspace_bytes.restype = S
         L.moe_get_layout.argtypes = [ctypes.POINTER(LayoutCfg)] + [P] * 9 + [S, P]
+        L.moe_get_layout_noalloc.argtypes = [ctypes.POINTER(LayoutCfg)] + [P] * 9
         L.moe_dispatch.argtypes = [ctypes.POINTER(DispatchCfg), P, P, P, P, P]
         L.moe_combine.argtypes = [ctypes.POINTER(CombineCfg), P, P, P, P, P]
         L.moe_quantize_e4m3.argtypes = [P, P, ctypes.c_int64, P]
@@ -89,7 +90,7 @@ def lib() -> ctypes.CDLL:
         L.moe_layer_workspace_bytes.restype = S
         L.moe_layer_forward.argtypes = ([ctypes.POINTER(MlpCfg), ctypes.c_int, ctypes.c_int] + [P] * 16 +
                                         [S, P])
-        for f in ("moe_route_topk", "moe_get_layout", "moe_dispatch", "moe_combine", "moe_quantize_e4m3",
+        for f in ("moe_route_topk", "moe_get_layout", "moe_get_layout_noalloc", "moe_dispatch", "moe_combine", "moe_quantize_e4m3",
                   "moe_dispatch_backward", "moe_combine_backward", "moe_route_dispatch", "moe_expert_up",
                   "moe_expert_down", "moe_layer_forward"):
             getattr(L, f).restype = ctypes.c_int
@@ -209,6 +210,28 @@ def get_layout(topk_idx, num_experts: int, num_ranks: int, capacity: int = 0, ou
                                 _ptr(lay.off_e), _ptr(lay.off_r), _ptr(lay.pos), _ptr(lay.recv_src),
                                 _ptr(lay.flags), _ptr(ws), ws.numel(), _stream(topk_idx.device)))
     return lay
+
+
+def get_layout_noalloc(topk_idx, num_experts: int, num_ranks: int, layout: Layout, capacity: int = 0,
+                       align_rows: int = 0) -> Layout:
+    """get_layout into caller-provided buffers (alloc_layout's Layout) with no
+    workspace: the library's own per-GPU count table is used, so nothing is
+    allocated.  Calls that may overlap on one GPU race on that table."""
+    torch = _torch()
+    _need(topk_idx, "topk_idx", torch.int32)
+    T, k = topk_idx.shape
+    dev = topk_idx.device
+    N = recv_rows(T, num_experts, k, capacity, align_rows)
+    for name, t, shape in (("cnt_e", layout.cnt_e, (num_experts,)), ("cnt_r", layout.cnt_r, (num_ranks,)),
+                           ("off_e", layout.off_e, (num_experts + 1,)), ("off_r", layout.off_r, (num_ranks + 1,)),
+                           ("pos", layout.pos, (T, k)), ("recv_src", layout.recv_src, (N,)),
+                           ("flags", layout.flags, (1,))):
+        _need(t, name, torch.int32, shape, dev)
+    cfg = LayoutCfg(T, num_experts, k, num_ranks, capacity, align_rows)
+    _check(lib().moe_get_layout_noalloc(ctypes.byref(cfg), _ptr(topk_idx), _ptr(layout.cnt_e), _ptr(layout.cnt_r),
+                                        _ptr(layout.off_e), _ptr(layout.off_r), _ptr(layout.pos),
+                                        _ptr(layout.recv_src), _ptr(layout.flags), _stream(dev)))
+    return layout
 
 
 def dispatch(x, pos, num_recv_rows: int, dtype: str = "fp8", recv_x=None, recv_scales=None,

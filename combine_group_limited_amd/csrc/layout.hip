@@ -19,8 +19,16 @@
 // its prefix, the totals and the exclusive scan over experts without another
 // launch, then writes pos / recv_src.  When one block covers all tokens both
 // passes run in a single launch with no workspace.
+#include <mutex>
+
 #include "moe_device.hpp"
 #include "moe_internal.hpp"
+
+// The count table of moe_get_layout_noalloc: a library-owned copy of the
+// layout workspace, one per GPU, held until the process ends.  Host code never
+// passes this name to a kernel (on the host it is only a stand-in for the
+// symbol); it uses the device address that hipGetSymbolAddress returns.
+static __device__ __align__(256) uint8_t scratch[cgl::kLayoutScratchBytes];
 
 namespace cgl {
 namespace {
@@ -356,5 +364,29 @@ hipError_t launch_layout(const int32_t* idx, int32_t* cnt_e, int32_t* cnt_r, int
 }
 
 size_t layout_lds_bytes_host(int E, int R) { return lds_bytes(E, R, true); }
+
+namespace {
+constexpr int kMaxScratchDevices = 256;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices];  // device address of `scratch`, per device ordinal
+}  // namespace
+
+hipError_t layout_scratch(void** ptr) {
+    int dev = 0;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess) return err;
+    if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        // first call on this device, which is current: look the symbol up once
+        void* p = nullptr;
+        err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (err != hipSuccess) return err;
+        if (!p) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return hipSuccess;
+}
 
 }  // namespace cgl

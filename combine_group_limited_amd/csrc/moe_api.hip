@@ -68,7 +68,7 @@ using namespace cgl;
 
 extern "C" {
 
-int32_t moe_abi_version(void) { return 5; }
+int32_t moe_abi_version(void) { return 6; }
 
 const char* moe_last_error(void) { return g_err; }
 
@@ -144,11 +144,12 @@ size_t moe_layout_workspace_bytes(const moe_layout_cfg* c) {
     return layout_workspace_bytes(c->num_tokens, c->num_experts, c->num_ranks);
 }
 
-moe_status moe_get_layout(const moe_layout_cfg* c, const int32_t* topk_idx, int32_t* cnt_e, int32_t* cnt_r,
-                          int32_t* off_e, int32_t* off_r, int32_t* pos, int32_t* recv_src, int32_t* flags,
-                          void* workspace, size_t workspace_bytes, void* stream) {
-    moe_status st = check_layout_cfg(c);
-    if (st != MOE_OK) return st;
+// Checks moe_get_layout's arrays (everything but the workspace).
+static_assert(kLayoutScratchBytes == MOE_LAYOUT_NOALLOC_MAX_BYTES, "header and library disagree");
+
+static moe_status check_layout_arrays(const moe_layout_cfg* c, const int32_t* topk_idx, const int32_t* cnt_e,
+                                      const int32_t* cnt_r, const int32_t* off_e, const int32_t* off_r,
+                                      const int32_t* pos, const int32_t* recv_src, const int32_t* flags) {
     const int T = c->num_tokens;
     if (!cnt_e || !cnt_r || !off_e || !off_r || !flags)
         return fail(MOE_ERR_INVALID, "layout: NULL output array");
@@ -159,6 +160,17 @@ moe_status moe_get_layout(const moe_layout_cfg* c, const int32_t* topk_idx, int3
     const void* ptrs[] = {topk_idx, cnt_e, cnt_r, off_e, off_r, pos, recv_src, flags};
     for (const void* p : ptrs)
         if (!aligned(p, 4)) return fail(MOE_ERR_INVALID, "layout: arrays must be 4-byte aligned");
+    return MOE_OK;
+}
+
+moe_status moe_get_layout(const moe_layout_cfg* c, const int32_t* topk_idx, int32_t* cnt_e, int32_t* cnt_r,
+                          int32_t* off_e, int32_t* off_r, int32_t* pos, int32_t* recv_src, int32_t* flags,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+    moe_status st = check_layout_cfg(c);
+    if (st != MOE_OK) return st;
+    if ((st = check_layout_arrays(c, topk_idx, cnt_e, cnt_r, off_e, off_r, pos, recv_src, flags)) != MOE_OK)
+        return st;
+    const int T = c->num_tokens;
     const size_t need = layout_workspace_bytes(T, c->num_experts, c->num_ranks);
     if (!workspace || workspace_bytes < need)
         return fail(MOE_ERR_WORKSPACE, "layout: workspace needs %zu bytes, got %zu", need,
@@ -168,6 +180,28 @@ moe_status moe_get_layout(const moe_layout_cfg* c, const int32_t* topk_idx, int3
                                     c->num_experts, c->topk, c->num_ranks, c->capacity, c->align_rows,
                                     (hipStream_t)stream),
                       "layout launch");
+}
+
+moe_status moe_get_layout_noalloc(const moe_layout_cfg* c, const int32_t* topk_idx, int32_t* cnt_e,
+                                  int32_t* cnt_r, int32_t* off_e, int32_t* off_r, int32_t* pos,
+                                  int32_t* recv_src, int32_t* flags, void* stream) {
+    moe_status st = check_layout_cfg(c);
+    if (st != MOE_OK) return st;
+    if ((st = check_layout_arrays(c, topk_idx, cnt_e, cnt_r, off_e, off_r, pos, recv_src, flags)) != MOE_OK)
+        return st;
+    const size_t need = layout_workspace_bytes(c->num_tokens, c->num_experts, c->num_ranks);
+    if (need > kLayoutScratchBytes)
+        return fail(MOE_ERR_WORKSPACE,
+                    "layout_noalloc: this shape needs %zu bytes of count table, above the library's fixed %zu "
+                    "(use moe_get_layout with a workspace)",
+                    need, (size_t)kLayoutScratchBytes);
+    void* ws = nullptr;  // the device address of this GPU's static count table
+    const hipError_t e = layout_scratch(&ws);
+    if (e != hipSuccess) return fail(MOE_ERR_HIP, "layout_noalloc: device scratch lookup: %s", hipGetErrorString(e));
+    return hip_status(launch_layout(topk_idx, cnt_e, cnt_r, off_e, off_r, pos, recv_src, flags, ws,
+                                    c->num_tokens, c->num_experts, c->topk, c->num_ranks, c->capacity,
+                                    c->align_rows, (hipStream_t)stream),
+                      "layout_noalloc launch");
 }
 
 static moe_status check_dispatch_cfg(const moe_dispatch_cfg* c) {

@@ -11,6 +11,10 @@ hipError_t launch_route(const float* logits, int32_t* idx, float* w, int T, int 
                         int n, int score_fn, int renorm, hipStream_t stream);
 
 size_t layout_workspace_bytes(int T, int E, int R);
+// moe_get_layout_noalloc's count table: a static device array of this size per
+// GPU; layout_scratch returns its address on the current device.
+constexpr size_t kLayoutScratchBytes = (size_t)1 << 20;
+hipError_t layout_scratch(void** ptr);
 size_t layout_lds_bytes_host(int E, int R);
 hipError_t launch_layout(const int32_t* idx, int32_t* cnt_e, int32_t* cnt_r, int32_t* off_e, int32_t* off_r,
                          int32_t* pos, int32_t* recv_src, int32_t* flags, void* workspace, int T, int E,

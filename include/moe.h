@@ -161,6 +161,29 @@ moe_status moe_get_layout(const moe_layout_cfg* cfg, const int32_t* topk_idx, in
                           size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ */
+/* moe_get_layout_noalloc -- moe_get_layout with no workspace argument, for  */
+/* callers that cannot allocate device memory (code under HIP graph capture,*/
+/* serving loops and harnesses that forbid allocation).                     */
+/*                                                                          */
+/* Same arguments (less the workspace), outputs, limits and errors as       */
+/* moe_get_layout.  The count table lives in a device array the library     */
+/* owns: MOE_LAYOUT_NOALLOC_MAX_BYTES per GPU, held from the first call on   */
+/* that GPU until the process ends.  Shapes whose                           */
+/* moe_layout_workspace_bytes(cfg) exceeds it return MOE_ERR_WORKSPACE       */
+/* before anything is enqueued (at E = 256, R = 32: above 231 936 tokens). */
+/* The call allocates and frees nothing; the stream must belong to the      */
+/* current device.  Every call on one GPU shares that GPU's array, so calls */
+/* that may overlap on one GPU (different streams, or host threads) race    */
+/* and give wrong results: serialise them, or use moe_get_layout with       */
+/* separate workspaces.  Nothing in the array needs clearing between calls. */
+/* ------------------------------------------------------------------------ */
+#define MOE_LAYOUT_NOALLOC_MAX_BYTES 1048576
+
+moe_status moe_get_layout_noalloc(const moe_layout_cfg* cfg, const int32_t* topk_idx, int32_t* cnt_e,
+                                  int32_t* cnt_r, int32_t* off_e, int32_t* off_r, int32_t* pos,
+                                  int32_t* recv_src, int32_t* flags, void* stream);
+
+/* ------------------------------------------------------------------------ */
 /* moe_dispatch -- scatter tokens into the expert-contiguous receive buffer. */
 /*                                                                          */
 /* Follows the Perplexity page, section "Dispatch": tokens are sent with    */
@@ -419,8 +442,9 @@ moe_status moe_quantize_e4m3(const float* in, uint8_t* out, int64_t n, void* str
 
 const char* moe_status_string(moe_status status);
 const char* moe_last_error(void);
-/* moe_abi_version: 5 (adds moe_layer_forward and moe_layer_workspace_bytes */
-/* to version 4; nothing earlier changed).                                  */
+/* moe_abi_version: 6 (adds moe_get_layout_noalloc to version 5, which     */
+/* added moe_layer_forward and moe_layer_workspace_bytes; nothing earlier   */
+/* changed).                                                                */
 int32_t moe_abi_version(void);
 
 #ifdef __cplusplus

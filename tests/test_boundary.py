@@ -37,7 +37,7 @@ def test_no_undefined_symbols_beyond_runtime():
 
 def test_status_strings_and_version():
     L = moe.lib()
-    assert L.moe_abi_version() == 5
+    assert L.moe_abi_version() == 6
     for s in (0, 1, 2, 4, 5):
         assert L.moe_status_string(s)
 
@@ -92,6 +92,24 @@ def test_layout_workspace_and_rejects():
     assert st == moe.MOE_ERR_WORKSPACE
     st = L.moe_get_layout(ctypes.byref(ok), *args, fake, 16, None)
     assert st == moe.MOE_ERR_WORKSPACE
+
+
+def test_layout_noalloc_rejects_before_any_hip_call():
+    """Bad configurations, missing arrays and shapes whose count table is
+    larger than the library's fixed array fail on the host."""
+    L = moe.lib()
+    fake = ctypes.c_void_p(1 << 20)
+    for vals in [(4, 256, 8, 33, 0, 0), (-1, 256, 8, 32, 0, 0), (4, 256, 8, 32, 4, 64)]:
+        cfg = moe.LayoutCfg(*vals)
+        assert L.moe_get_layout_noalloc(ctypes.byref(cfg), *([fake] * 8), None) == moe.MOE_ERR_INVALID
+    ok = moe.LayoutCfg(4096, 256, 8, 32, 0, 0)
+    assert L.moe_get_layout_noalloc(ctypes.byref(ok), *([None] * 8), None) == moe.MOE_ERR_INVALID
+    big = moe.LayoutCfg(231937, 256, 8, 32, 0, 0)
+    assert L.moe_layout_workspace_bytes(ctypes.byref(big)) > 1 << 20
+    assert L.moe_get_layout_noalloc(ctypes.byref(big), *([fake] * 8), None) == moe.MOE_ERR_WORKSPACE
+    assert b"count table" in L.moe_last_error()
+    fits = moe.LayoutCfg(231936, 256, 8, 32, 0, 0)
+    assert L.moe_layout_workspace_bytes(ctypes.byref(fits)) <= 1 << 20
 
 
 def test_dispatch_rejects():
