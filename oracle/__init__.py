@@ -40,11 +40,17 @@ _lib = None
 
 
 def lib():
+    """The compiled oracle.  CGL_ORACLE_LIB names another build of the same
+    source to load instead (the mutation test points it at deliberately
+    broken copies to show that the pins catch them)."""
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
-            build()
-        L = ctypes.CDLL(_LIB)
+        path = os.environ.get("CGL_ORACLE_LIB")
+        if not path:
+            path = _LIB
+            if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+                build()
+        L = ctypes.CDLL(path)
         P = ctypes.c_void_p
         i32, i64 = ctypes.c_int, ctypes.c_int64
         L.orc_exp_r.restype = ctypes.c_float
