@@ -231,12 +231,13 @@ def _ranges(start, count):
     return (np.ascontiguousarray(start, dtype=np.int32), np.ascontiguousarray(count, dtype=np.int32))
 
 
-def mlp_up(x, xs, w1, w1s, start, count, rows=None, act=None, act_s=None, want_f64=False):
+def mlp_up(x, xs, w1, w1s, start, count, rows=None, act=None, act_s=None, want_f64=False, act_f64=None):
     """Expert up projection + SwiGLU + FP8 (power-of-two scale) quantisation.
 
     x uint8 [N,H], xs f32 [N,H/128], w1 uint8 [E,2I,H], w1s f32 [E,2I/128,H/128];
     start/count int32 [E].  Returns (act uint8 [N,I], act_s f32 [N,I/128],
-    act_f64 [N,I] or None); rows not computed keep the arrays passed in."""
+    act_f64 [N,I] or None): the unrounded SwiGLU output, when want_f64 or an
+    act_f64 array is given; rows not computed keep the arrays passed in."""
     x = np.ascontiguousarray(x, dtype=np.uint8)
     xs = np.ascontiguousarray(xs, dtype=np.float32)
     w1 = np.ascontiguousarray(w1, dtype=np.uint8)
@@ -247,7 +248,9 @@ def mlp_up(x, xs, w1, w1s, start, count, rows=None, act=None, act_s=None, want_f
     st, ct = _ranges(start, count)
     act = np.zeros((N, I), np.uint8) if act is None else act
     act_s = np.zeros((N, I // 128), np.float32) if act_s is None else act_s
-    f64 = np.full((N, I), np.nan) if want_f64 else None
+    f64 = act_f64 if act_f64 is not None else (np.full((N, I), np.nan) if want_f64 else None)
+    if f64 is not None:
+        assert f64.shape == (N, I) and f64.dtype == np.float64 and f64.flags["C_CONTIGUOUS"]
     r = None if rows is None else np.ascontiguousarray(rows, dtype=np.int32)
     rc = lib().orc_mlp_up(N, H, I, E, _p(st), _p(ct), 0 if r is None else r.size,
                           None if r is None else _p(r), _p(x), _p(xs), _p(w1), _p(w1s), _p(act),

@@ -1,29 +1,7 @@
 """GPU parity of the expert MLP (moe_expert_up, moe_expert_down) through the C
-ABI against the oracle.
-
-Both sides read the same FP8 codes and power-of-two scales.  The GPU sums on
-the matrix cores, the oracle in double, so results are compared within
-bounds derived from the arithmetic.  The matrix cores' FP8 dot product is not
-sequential fp32: within one 64-deep step the products are aligned to the
-largest and the bits below 2^-13 of it are dropped, toward zero (measured on
-gfx950: a product 2^-14 of the largest vanishes, 1.5*2^-13 of it becomes
-2^-13), so each step can lose up to 64 * 2^-13 * max|p|; the bounds add
-al = K 2^-12 max_k |a_k w_k| per output (one bit of margin) to the fp32
-terms below:
-  up:   |dq_gpu - act| <= 2^-4 (|act| + d) + 2^-10 s_gpu + d, where
-        d = 1.1 |u| dh + |silu(g)| dh + (|g| 2^-24 + 2^-20) |act| bounds the
-        error of the activation (dh = K 2^-24 sum_k |x_k w_k| + al, the worst
-        case of an fp32 sum of K terms plus the alignment loss; the last term
-        covers SwiGLU itself,
-        evaluated with the hardware exp2 and reciprocal, 1 ulp each, on the
-        rounded product -g log2(e)) and the rest is the E4M3 rounding of a
-        value with power-of-two scale s (half a step, 2^-10 s below the
-        normals);
-        scales must agree except where the fp32 row maximum crossed a power
-        of two (then by exactly a factor 2);
-  down: |y_gpu - y| <= 2^-8 |y| + 2^-8 |y_gpu| + 2 K 2^-24 sum_k |a_k w_k| + al
-        (one bf16 rounding on each side, the fp32 sum and the alignment loss).
-Rows outside every expert's range must stay untouched.
+ABI against the oracle, within the bounds of ``bounds`` (the GPU sums on
+the matrix cores in fp32, the oracle in double).  Rows outside every expert's
+range must stay untouched.
 """
 import sys
 
@@ -39,10 +17,9 @@ if not torch.cuda.is_available():
     pytest.skip("needs a GPU", allow_module_level=True)
 
 import combine_group_limited_amd as moe  # noqa: E402
-import oracle  # noqa: E402
+from bounds import check_down, check_up, tile_rows  # noqa: E402
 
 DEV = torch.device("cuda:0")
-E4M3 = np.array([oracle.e4m3_value(c) for c in range(256)])
 
 
 def say(*a):
@@ -54,12 +31,6 @@ def dev(a):
     return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
 
 
-def deq(codes, scales, block_rows=1):
-    v = E4M3[codes]
-    s = np.repeat(np.repeat(scales.astype(np.float64), 128, axis=-1), block_rows, axis=-2)
-    return v * s
-
-
 def layout_arrays(start, count, capacity=0):
     E = len(count)
     off = np.zeros(E + 1, np.int32)
@@ -67,63 +38,6 @@ def layout_arrays(start, count, capacity=0):
         off[:E] = start
         off[E] = start[-1] + count[-1]
     return count.astype(np.int32), off
-
-
-def check_up(x, xs, w1, w1s, start, count, act_g, act_s_g, rows):
-    """Bounds of the module docstring on the given rows (numpy for the bound
-    terms only; the reference values are the oracle's)."""
-    I = w1.shape[1] // 2
-    H = x.shape[1]
-    ref_a, ref_s, f64 = oracle.mlp_up(x, xs, w1, w1s, start, count, rows=rows, want_f64=True)
-    xd = deq(x[rows], xs[rows])
-    wd = {}
-    e_of = np.array([np.nonzero((r >= start) & (r < start + count))[0][0] for r in rows])
-    nbad = 0
-    code_eq = 0
-    scale_eq = 0
-    for i, r in enumerate(rows):
-        e = e_of[i]
-        if e not in wd:
-            wd[e] = deq(w1[e], w1s[e], block_rows=128)
-        h = wd[e] @ xd[i]
-        S = np.abs(wd[e]) @ np.abs(xd[i])
-        al = H * 2.0 ** -12 * np.max(np.abs(wd[e]) * np.abs(xd[i])[None, :], axis=1)
-        dh = H * 2.0 ** -24 * S + al
-        g, u = h[:I], h[I:]
-        silu = g / (1.0 + np.exp(-g))
-        a = f64[r]
-        d = 1.1 * np.abs(u) * dh[:I] + np.abs(silu) * dh[I:] + (np.abs(g) * 2.0 ** -24 + 2.0 ** -20) * np.abs(a)
-        s_g = np.repeat(act_s_g[r].astype(np.float64), 128)
-        dq = E4M3[act_g[r]] * s_g
-        bound = 2.0 ** -4 * (np.abs(a) + d) + 2.0 ** -10 * s_g + d
-        nbad += int(np.sum(np.abs(dq - a) > bound))
-        ratio = act_s_g[r] / ref_s[r]
-        assert np.all((ratio == 1.0) | (ratio == 2.0) | (ratio == 0.5)), (r, ratio)
-        scale_eq += int(np.sum(ratio == 1.0))
-        code_eq += int(np.sum(act_g[r] == ref_a[r]))
-    n = len(rows)
-    return nbad, code_eq / (n * I), scale_eq / (n * (I // 128))
-
-
-def check_down(act, act_s, w2, w2s, start, count, y_g_bits, rows):
-    K = act.shape[1]
-    ref = oracle.mlp_down(act, act_s, w2, w2s, start, count, rows=rows)
-    ad = deq(act[rows], act_s[rows])
-    wd = {}
-    nbad = 0
-    exact = 0
-    for i, r in enumerate(rows):
-        e = np.nonzero((r >= start) & (r < start + count))[0][0]
-        if e not in wd:
-            wd[e] = deq(w2[e], w2s[e], block_rows=128)
-        S = np.abs(wd[e]) @ np.abs(ad[i])
-        al = K * 2.0 ** -12 * np.max(np.abs(wd[e]) * np.abs(ad[i])[None, :], axis=1)
-        yr = W.bf16_bits_to_f32(ref[r]).astype(np.float64)
-        yg = W.bf16_bits_to_f32(y_g_bits[r]).astype(np.float64)
-        bound = 2.0 ** -8 * (np.abs(yr) + np.abs(yg)) + 2 * K * 2.0 ** -24 * S + al
-        nbad += int(np.sum(np.abs(yg - yr) > bound))
-        exact += int(np.sum(y_g_bits[r] == ref[r]))
-    return nbad, exact / (len(rows) * y_g_bits.shape[1])
 
 
 def run_mlp(wl, start, count, capacity=0, rows=None, cnt_override=None):
@@ -143,8 +57,10 @@ def run_mlp(wl, start, count, capacity=0, rows=None, cnt_override=None):
         covered[s:s + c] = True
     all_rows = np.nonzero(covered)[0].astype(np.int32)
     rows = all_rows if rows is None else rows
-    # untouched rows keep the sentinel
+    # untouched rows keep the sentinel; every covered row got every scale
+    # (a power of two, never the negative sentinel)
     assert np.all(act_g[~covered] == 0xEE) and np.all(act_s_g[~covered] == -3.0)
+    assert np.all(act_s_g[covered] > 0)
     nbad, code_eq, scale_eq = check_up(x, xs, w1, w1s, start, count, act_g, act_s_g, rows)
     say(f"   up {wl.name}: {len(rows)} rows, codes equal {code_eq:.5f}, scales equal {scale_eq:.5f}, "
         f"out of bound {nbad}")
@@ -154,6 +70,7 @@ def run_mlp(wl, start, count, capacity=0, rows=None, cnt_override=None):
     moe.expert_down(act, act_s, dev(w2), dev(w2s), dev(cnt), dev(off), capacity, y)
     yb = y.view(torch.int16).cpu().numpy().view(np.uint16)
     assert np.all(yb[~covered] == 1234)
+    assert not np.any(yb[covered] == 1234)   # values of order one: the sentinel means unwritten
     nbad, exact = check_down(act_g, act_s_g, w2, w2s, start, count, yb, rows)
     say(f"   down {wl.name}: exact {exact:.5f}, out of bound {nbad}")
     assert nbad == 0 and exact > 0.9
@@ -213,16 +130,15 @@ def test_mlp_many_experts():
 
 def test_mlp_rank_full_size_sampled():
     """One expert-parallel rank of the DeepSeek-V3 shape (8 experts, 32768
-    rows, H 7168, I 2048) in the benchmark's launch configuration; 24 rows
-    spread over all experts checked against the oracle."""
+    rows, H 7168, I 2048) in the benchmark's launch configuration; one row in
+    every 128-row tile of every expert (so every 128- or 256-row tile the
+    kernels use), each expert's first and last row, checked against the oracle."""
     wl = W.MLP_WORKLOADS["mlp_rank"]
     say(f"[gpu] mlp full size {wl}")
     start, count, _ = W.mlp_ranges(wl)
-    rng = np.random.default_rng(1)
-    rows = []
-    for s, c in zip(start, count):
-        rows += [s, s + c - 1, int(rng.integers(s, s + c))]
-    run_mlp(wl, start, count, rows=np.array(sorted(rows), np.int32))
+    rows = np.union1d(tile_rows(start, count, 128, seed=1), start[count > 0]).astype(np.int32)
+    say(f"   {len(rows)} rows sampled")
+    run_mlp(wl, start, count, rows=rows)
 
 
 @pytest.mark.parametrize("N,H,I,E", [(4096, 1024, 512, 2), (1100, 640, 256, 2)])

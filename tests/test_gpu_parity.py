@@ -25,6 +25,7 @@ if not torch.cuda.is_available():
 
 import combine_group_limited_amd as moe  # noqa: E402
 import oracle  # noqa: E402
+from bounds import combine_check  # noqa: E402
 
 DEV = torch.device("cuda:0")
 HELPERS = os.path.join(os.path.dirname(__file__), "helpers")
@@ -45,23 +46,6 @@ def bf16_from_dev(t):
 
 def sf(wl):
     return oracle.SOFTMAX if wl.score == "softmax" else oracle.SIGMOID
-
-
-def combine_check(got_bits, ref_bits, y_bits, pos, w):
-    got = W.bf16_bits_to_f32(got_bits).astype(np.float64)
-    ref = W.bf16_bits_to_f32(ref_bits).astype(np.float64)
-    T, k = pos.shape
-    yf = W.bf16_bits_to_f32(y_bits)
-    mag = np.zeros_like(ref)
-    for j in range(k):
-        p = pos[:, j]
-        ok = p >= 0
-        mag[ok] += np.abs(w[ok, j:j + 1].astype(np.float64) * yf[p[ok]].astype(np.float64))
-    bound = 1e-2 * np.abs(ref) + 2 * k * 2.0 ** -24 * mag
-    bad = np.abs(got - ref) > bound
-    big = np.abs(ref) >= 1e-2
-    rel = np.abs(got - ref)[big] / np.abs(ref)[big]
-    return int(bad.sum()), float(rel.max() if rel.size else 0.0), float(np.mean(got == ref))
 
 
 # --------------------------------------------------------------------------
