@@ -22,7 +22,7 @@ LIB_PATH = os.path.join(PKG, "libcgl_moe.so")
 MOE_OK, MOE_ERR_INVALID, MOE_ERR_WORKSPACE, MOE_ERR_UNSUPPORTED, MOE_ERR_HIP = 0, 1, 2, 4, 5
 SCORE_FNS = {"sigmoid": 0, "softmax": 1}
 DISPATCH_DTYPES = {"fp8": 0, "bf16": 1, "fp8_pow2": 2}
-FLAG_CAPACITY_OVERFLOW, FLAG_BAD_INDEX = 1, 2
+FLAG_CAPACITY_OVERFLOW, FLAG_BAD_INDEX, FLAG_INCOMPLETE, FLAG_BAD_SCALE = 1, 2, 4, 8
 
 
 class MoeError(RuntimeError):
@@ -78,6 +78,7 @@ def lib() -> ctypes.CDLL:
         L.moe_dispatch.argtypes = [ctypes.POINTER(DispatchCfg), P, P, P, P, P]
         L.moe_combine.argtypes = [ctypes.POINTER(CombineCfg), P, P, P, P, P]
         L.moe_quantize_e4m3.argtypes = [P, P, ctypes.c_int64, P]
+        L.moe_check_pow2_scales.argtypes = [P, ctypes.c_int64, P, P]
         L.moe_dispatch_backward.argtypes = [ctypes.POINTER(CombineCfg), P, P, P, P]
         L.moe_combine_backward.argtypes = [ctypes.POINTER(CombineCfg), P, P, P, P, P, P, P]
         L.moe_route_dispatch_workspace_bytes.argtypes = []
@@ -91,6 +92,7 @@ def lib() -> ctypes.CDLL:
         L.moe_layer_forward.argtypes = ([ctypes.POINTER(MlpCfg), ctypes.c_int, ctypes.c_int] + [P] * 16 +
                                         [S, P])
         for f in ("moe_route_topk", "moe_get_layout", "moe_get_layout_noalloc", "moe_dispatch", "moe_combine", "moe_quantize_e4m3",
+                  "moe_check_pow2_scales",
                   "moe_dispatch_backward", "moe_combine_backward", "moe_route_dispatch", "moe_expert_up",
                   "moe_expert_down", "moe_layer_forward"):
             getattr(L, f).restype = ctypes.c_int
@@ -449,6 +451,21 @@ def layer_forward(x, pos, topk_w, cnt_e, off_e, w1, w1_scales, w2, w2_scales, nu
 _layer_ws = {}
 
 
+def barrier_gave_up(workspace) -> int:
+    """Word 2 of a route_dispatch or layer_forward barrier workspace (waits for
+    the device): the number of blocks that stopped waiting at a barrier.
+    Nonzero means the outputs of the call that raised it, and of every later
+    call on that workspace, are incomplete until reset_barrier_workspace()."""
+    return int(workspace.view(_torch().int32)[2].item())
+
+
+def reset_barrier_workspace(workspace):
+    """Zero a barrier workspace (on the current stream) so that it can be used
+    again after a give-up."""
+    workspace.zero_()
+    return workspace
+
+
 def combine(y, pos, topk_w, out=None, units_per_wave: int = 0):
     """y bf16 [N,H], pos int32 [T,k], topk_w fp32 [T,k] -> out bf16 [T,H]."""
     torch = _torch()
@@ -509,6 +526,21 @@ def combine_backward(grad_out, y, pos, topk_w, grad_y=None, grad_w=None, units_p
     return grad_y, grad_w
 
 
+def check_pow2_scales(*scales) -> bool:
+    """True if every element of the given fp32 GPU tensors is a positive normal
+    power of two, the precondition of expert_up, expert_down and layer_forward
+    on their block scales (waits for the device)."""
+    torch = _torch()
+    if not scales:
+        return True
+    dev = scales[0].device
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    for i, t in enumerate(scales):
+        _need(t, f"scales[{i}]", torch.float32, device=dev)
+        _check(lib().moe_check_pow2_scales(_ptr(t), t.numel(), _ptr(status), _stream(dev)))
+    return int(status.item()) & FLAG_BAD_SCALE == 0
+
+
 def quantize_e4m3(x, out=None):
     """fp32 tensor -> uint8 E4M3FN codes of the same shape."""
     torch = _torch()
@@ -521,5 +553,8 @@ def quantize_e4m3(x, out=None):
     return out
 
 
-__all__ = ["lib", "route_topk", "get_layout", "alloc_layout", "layout_workspace_bytes", "dispatch",
-           "combine", "dispatch_backward", "combine_backward", "quantize_e4m3", "Layout", "MoeError", "FLAG_CAPACITY_OVERFLOW", "FLAG_BAD_INDEX"]
+__all__ = ["lib", "MoeError", "Layout", "route_topk", "get_layout", "get_layout_noalloc", "alloc_layout",
+           "layout_workspace_bytes", "recv_rows", "dispatch", "combine", "dispatch_backward", "combine_backward",
+           "route_dispatch", "route_dispatch_workspace", "expert_up", "expert_down", "layer_forward",
+           "layer_workspace", "barrier_gave_up", "reset_barrier_workspace", "check_pow2_scales", "quantize_e4m3",
+           "FLAG_CAPACITY_OVERFLOW", "FLAG_BAD_INDEX", "FLAG_INCOMPLETE", "FLAG_BAD_SCALE"]

@@ -42,6 +42,7 @@ constexpr int kFusedThreads = 256;
 constexpr int kFusedWaves = kFusedThreads / kWave;
 constexpr int kUnitChannels = 512;  // one 16-byte load per lane
 constexpr int kSliceRows = 2048;    // recv_src rows per LDS slice
+constexpr int kFlagIncomplete = 4;  // MOE_FLAG_INCOMPLETE
 
 struct FusedArgs {
     RouteArgs r;  // logits -> idx [T,k], w [T,k]; T, E, G, g, k, n, score_fn, renorm
@@ -107,6 +108,9 @@ __global__ __launch_bounds__(kFusedThreads) void fused_decode_kernel(FusedArgs a
     const int nw = gridDim.x * kFusedWaves;
     const int items = T * a.units;
 
+    // a workspace an earlier launch gave up on is refused at the barrier
+    const bool refused = tid == 0 && barrier_gave_up(a.bar);
+
     // ---- 1. first unit of x (independent of the routing), then routing ----
     u32x4 v0 = u32x4{0u, 0u, 0u, 0u};
     if (gw < items) v0 = load_unit(a, gw, lane);
@@ -115,7 +119,13 @@ __global__ __launch_bounds__(kFusedThreads) void fused_decode_kernel(FusedArgs a
     const u32x2 q0 = quantize(a, v0, s0);
 
     // ---- 2. every token routed ---------------------------------------------
-    if (!grid_barrier<false>(a.bar)) return;  // block-uniform
+    if (!grid_barrier<false>(a.bar, refused)) {  // block-uniform
+        // block 0 writes the flags only here or at its end, never both
+        if (blockIdx.x == 0 && tid == 0) a.flags[0] = kFlagIncomplete;
+        return;
+    }
+    // a block of this launch that stopped waiting as the barrier opened
+    const bool gave_up = blockIdx.x == 0 && tid == 0 && barrier_gave_up(a.bar);
 
     // ---- 3. the layout of the whole batch, in LDS ----------------------------
     for (int i = tid; i < a.nch * E; i += kFusedThreads) emask[i] = 0;
@@ -185,7 +195,7 @@ __global__ __launch_bounds__(kFusedThreads) void fused_decode_kernel(FusedArgs a
         if (a.C > 0)
             for (int e = tid; e < E; e += kFusedThreads) over |= tot[e] > a.C;
         const int any_over = __syncthreads_or(over);
-        if (tid == 0) a.flags[0] = (any_over ? 1 : 0) | (any_bad ? 2 : 0);
+        if (tid == 0) a.flags[0] = (any_over ? 1 : 0) | (any_bad ? 2 : 0) | (gave_up ? kFlagIncomplete : 0);
     }
     const int pairs = T * k;
     const int per = (pairs + gridDim.x - 1) / gridDim.x;

@@ -184,24 +184,26 @@ template <int TM, int NRU, int NRD>
 __global__ __launch_bounds__(kLayerThreads) void layer_kernel(LayerArgs a) {
     const int waves = gridDim.x * (kLayerThreads / kWave);
     const int w0 = blockIdx.x * (kLayerThreads / kWave) + wave_in_block();
+    // a workspace an earlier launch gave up on is refused at the first barrier
+    const bool refused = threadIdx.x == 0 && barrier_gave_up(a.bar);
     stamp(a.bar, 0);
 
     layer_dispatch<kLayerUnits>(a.d, w0, waves);
-    if (!grid_barrier<true>(a.bar)) return;  // block-uniform
+    if (!grid_barrier<true>(a.bar, refused)) return;  // block-uniform
     stamp(a.bar, 1);
 
     for (unsigned b = blockIdx.x; b < a.up_blocks; b += gridDim.x) {
         mlp_block<true, TM, NRU, true>(a.up, (int)b);
         __syncthreads();  // the next tile rewrites the LDS this one read last
     }
-    if (!grid_barrier<true>(a.bar)) return;
+    if (!grid_barrier<true>(a.bar, false)) return;
     stamp(a.bar, 2);
 
     for (unsigned b = blockIdx.x; b < a.down_blocks; b += gridDim.x) {
         mlp_block<false, TM, NRD, true>(a.down, (int)b);
         __syncthreads();
     }
-    if (!grid_barrier<true>(a.bar)) return;
+    if (!grid_barrier<true>(a.bar, false)) return;
     stamp(a.bar, 3);
 
     layer_combine<kLayerCombineUnits>(a.c, w0, waves);

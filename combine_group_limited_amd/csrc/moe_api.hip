@@ -53,7 +53,27 @@ __global__ __launch_bounds__(256) void quantize_e4m3_kernel(const float* in, uin
     }
 }
 
+// *status |= MOE_FLAG_BAD_SCALE if any s[i] is not a positive normal power
+// of two (sign 0, exponent field 1..254, mantissa 0): one atomic per wave
+// that saw one, none otherwise.
+__global__ __launch_bounds__(256) void check_pow2_kernel(const float* s, int64_t n, int32_t* status) {
+    bool bad = false;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+        const uint32_t b = __float_as_uint(s[i]);
+        const uint32_t ex = (b >> 23) & 0xFFu;
+        bad |= (b & 0x807FFFFFu) != 0u || ex == 0u || ex == 0xFFu;
+    }
+    const uint64_t any = __ballot(bad);  // every lane of the wave is active here
+    if (any != 0u && (threadIdx.x & 63) == 0) atomicOr(status, MOE_FLAG_BAD_SCALE);
+}
+
 }  // namespace
+
+hipError_t launch_check_pow2(const float* s, int64_t n, int32_t* status, hipStream_t stream) {
+    const int64_t blocks = (n + 255) / 256 < 1024 ? (n + 255) / 256 : 1024;
+    hipLaunchKernelGGL(check_pow2_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, s, n, status);
+    return hipGetLastError();
+}
 
 hipError_t launch_quantize_e4m3(const float* in, uint8_t* out, int64_t n, hipStream_t stream) {
     const int64_t quads = (n + 3) / 4;
@@ -68,7 +88,7 @@ using namespace cgl;
 
 extern "C" {
 
-int32_t moe_abi_version(void) { return 6; }
+int32_t moe_abi_version(void) { return 7; }
 
 const char* moe_last_error(void) { return g_err; }
 
@@ -447,6 +467,15 @@ moe_status moe_layer_forward(const moe_mlp_cfg* c, int num_tokens, int topk, con
                                    act, act_scales, y, out, (uint32_t*)workspace, T, k, N, H, I, E, c->capacity,
                                    (hipStream_t)stream),
                       "layer_forward launch");
+}
+
+moe_status moe_check_pow2_scales(const float* scales, int64_t n, int32_t* status, void* stream) {
+    if (n < 0) return fail(MOE_ERR_INVALID, "check_pow2_scales: n < 0");
+    if (!status) return fail(MOE_ERR_INVALID, "check_pow2_scales: NULL status");
+    if (!aligned(status, 4)) return fail(MOE_ERR_INVALID, "check_pow2_scales: status must be 4-byte aligned");
+    if (n == 0) return ok();
+    if (!scales || !aligned(scales, 4)) return fail(MOE_ERR_INVALID, "check_pow2_scales: scales NULL or unaligned");
+    return hip_status(launch_check_pow2(scales, n, status, (hipStream_t)stream), "check_pow2_scales launch");
 }
 
 moe_status moe_quantize_e4m3(const float* in, uint8_t* out, int64_t n, void* stream) {

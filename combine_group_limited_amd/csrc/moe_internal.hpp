@@ -63,5 +63,6 @@ hipError_t launch_expert_down(const int32_t* cnt_e, const int32_t* off_e, const 
                               hipStream_t stream);
 
 hipError_t launch_quantize_e4m3(const float* in, uint8_t* out, int64_t n, hipStream_t stream);
+hipError_t launch_check_pow2(const float* s, int64_t n, int32_t* status, hipStream_t stream);
 
 }  // namespace cgl

@@ -62,6 +62,10 @@ typedef enum {
 /* Bits of the *flags word written by moe_get_layout. */
 #define MOE_FLAG_CAPACITY_OVERFLOW 1  /* padded mode: some expert got more than C pairs */
 #define MOE_FLAG_BAD_INDEX 2          /* an index outside [0,E) or repeated in a token */
+#define MOE_FLAG_BAD_SCALE 8          /* moe_check_pow2_scales: a scale that is not a  */
+                                      /* positive normal power of two                   */
+#define MOE_FLAG_INCOMPLETE 4         /* moe_route_dispatch only: the launch did not   */
+                                      /* complete (barrier give-up; see there)          */
 
 /* ------------------------------------------------------------------------ */
 /* moe_route_topk -- group-limited top-k gating.                            */
@@ -309,10 +313,14 @@ moe_status moe_combine_backward(const moe_combine_cfg* cfg, const uint16_t* grad
 /* every call leaves the counters at zero, so it needs no clearing between  */
 /* calls.                                                                   */
 /* Calls that may run at the same time (different streams) need different   */
-/* workspaces.  Its third 32-bit word counts blocks that stopped waiting at */
-/* the barrier after about a second (which only happens if the GPU cannot   */
-/* hold the whole grid at once); it stays 0 in normal use, and the outputs  */
-/* of a call that raised it are incomplete.                                 */
+/* workspaces.  Its third 32-bit word (word 2) counts blocks that stopped   */
+/* waiting at the barrier after about a second, which only happens if the  */
+/* GPU cannot hold the whole grid at once.  It stays 0 in normal use.  Once */
+/* it is nonzero the library never clears it: that call and every later    */
+/* call on the workspace write MOE_FLAG_INCOMPLETE into flags[0] and leave  */
+/* the other outputs incomplete (a refused call does not wait or count at   */
+/* the barrier, so stray counts a give-up left behind are never used),      */
+/* until the caller zeroes the workspace again.                             */
 /* Limits: those of the three calls, and T <= 1024 with                     */
 /*   8*ceil(T/64)*(E+R) + 4*(2E + 1 + T*k + 2048) <= 64512 bytes of LDS;     */
 /*   larger shapes return MOE_ERR_UNSUPPORTED (use the three calls).        */
@@ -343,10 +351,13 @@ moe_status moe_route_dispatch(const moe_route_cfg* route, const moe_layout_cfg* 
 /* arrays moe_get_layout writes).  Rows outside every range are not         */
 /* written.  A layout whose ranges leave [0, N) makes that expert skipped.  */
 /* All operands are OCP E4M3FN codes with POWER-OF-TWO fp32 block scales    */
-/* (only the exponent bits are used; a scale that is not a power of two    */
-/* gives wrong results): activations one scale per row and 128 columns, as  */
-/* moe_dispatch(MOE_DISPATCH_FP8_E4M3_POW2) writes them; weights one per    */
-/* 128x128 block.  Accumulation is fp32 on the matrix cores.                */
+/* (the matrix cores take only the exponent bits, so a scale that is not a  */
+/* positive normal power of two gives wrong results and is NOT checked here:*/
+/* run moe_check_pow2_scales on the weight scales once when they are        */
+/* loaded; activation scales that moe_dispatch(MOE_DISPATCH_FP8_E4M3_POW2)  */
+/* or moe_expert_up wrote are powers of two by construction): activations  */
+/* one scale per row and 128 columns; weights one per 128x128 block.        */
+/* Accumulation is fp32 on the matrix cores.                                */
 /*                                                                          */
 /* moe_expert_up:                                                           */
 /*   h[p, n]   = sum_k x(p,k) * w1(e,n,k), n < 2I (rows 0..I-1 gate, I..2I-1 */
@@ -408,10 +419,15 @@ moe_status moe_expert_down(const moe_mlp_cfg* cfg, const int32_t* cnt_e, const i
 /* workspace: at least moe_layer_workspace_bytes() of device memory,        */
 /* 16-byte aligned, ZEROED BEFORE ITS FIRST USE; the barriers leave it at   */
 /* rest after every call.  Calls that may run at the same time need         */
-/* different workspaces.  Its third 32-bit word counts blocks that stopped  */
-/* waiting at a barrier after about a second (only if the GPU cannot hold   */
-/* the whole grid, e.g. while other kernels occupy it); it stays 0 in       */
-/* normal use, and the outputs of a call that raised it are incomplete.    */
+/* different workspaces.  Its third 32-bit word (word 2) counts blocks that */
+/* stopped waiting at a barrier after about a second (only if the GPU       */
+/* cannot hold the whole grid, e.g. while other kernels occupy it); it      */
+/* stays 0 in normal use.  Once nonzero it is never cleared by the library: */
+/* the outputs of that call and of every later call on the workspace are    */
+/* incomplete (later calls are refused at the first barrier, so stray       */
+/* counts a give-up left behind are never used) until the caller zeroes the */
+/* workspace again.  Read word 2 after the call to know (e.g. the Python    */
+/* binding's barrier_gave_up()).                                            */
 /* Words 768..775 receive, as four 64-bit values (low word first), the     */
 /* GPU's constant 100-MHz clock (s_memrealtime) read by block 0 at the      */
 /* start and after each barrier: phase timings, for diagnostics only.       */
@@ -433,6 +449,17 @@ moe_status moe_layer_forward(const moe_mlp_cfg* cfg, int num_tokens, int topk, c
                              uint16_t* out, void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ */
+/* moe_check_pow2_scales -- checks the precondition of the expert MLP and   */
+/* the one-launch layer on their fp32 block scales: ORs MOE_FLAG_BAD_SCALE  */
+/* into *status (device int32, never cleared by the library) if any of      */
+/* scales[0..n) is not a positive normal power of two (sign 0, exponent     */
+/* field 1..254, mantissa 0).  Asynchronous like every call: read *status   */
+/* after the stream has reached it.  n >= 0; scales and status 4-byte       */
+/* aligned device pointers.                                                 */
+/* ------------------------------------------------------------------------ */
+moe_status moe_check_pow2_scales(const float* scales, int64_t n, int32_t* status, void* stream);
+
+/* ------------------------------------------------------------------------ */
 /* moe_quantize_e4m3 -- the element conversion moe_dispatch uses, exposed   */
 /* on its own: out[i] = E4M3FN nearest-even of in[i], magnitudes above 448  */
 /* saturate to 448, sign kept (codes for NaN inputs are unspecified).       */
@@ -442,9 +469,10 @@ moe_status moe_quantize_e4m3(const float* in, uint8_t* out, int64_t n, void* str
 
 const char* moe_status_string(moe_status status);
 const char* moe_last_error(void);
-/* moe_abi_version: 6 (adds moe_get_layout_noalloc to version 5, which     */
-/* added moe_layer_forward and moe_layer_workspace_bytes; nothing earlier   */
-/* changed).                                                                */
+/* moe_abi_version: 7 (adds moe_check_pow2_scales and the                  */
+/* MOE_FLAG_INCOMPLETE report of moe_route_dispatch to version 6, which     */
+/* added moe_get_layout_noalloc; version 5 added moe_layer_forward and      */
+/* moe_layer_workspace_bytes; no signature changed).                        */
 int32_t moe_abi_version(void);
 
 #ifdef __cplusplus

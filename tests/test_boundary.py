@@ -37,7 +37,7 @@ def test_no_undefined_symbols_beyond_runtime():
 
 def test_status_strings_and_version():
     L = moe.lib()
-    assert L.moe_abi_version() == 6
+    assert L.moe_abi_version() == 7
     for s in (0, 1, 2, 4, 5):
         assert L.moe_status_string(s)
 
@@ -110,6 +110,17 @@ def test_layout_noalloc_rejects_before_any_hip_call():
     assert b"count table" in L.moe_last_error()
     fits = moe.LayoutCfg(231936, 256, 8, 32, 0, 0)
     assert L.moe_layout_workspace_bytes(ctypes.byref(fits)) <= 1 << 20
+
+
+def test_check_pow2_scales_rejects():
+    L = moe.lib()
+    fake = ctypes.c_void_p(1 << 20)
+    L.moe_check_pow2_scales.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
+    assert L.moe_check_pow2_scales(fake, -1, fake, None) == moe.MOE_ERR_INVALID
+    assert L.moe_check_pow2_scales(fake, 10, None, None) == moe.MOE_ERR_INVALID
+    assert L.moe_check_pow2_scales(None, 10, fake, None) == moe.MOE_ERR_INVALID
+    assert L.moe_check_pow2_scales(ctypes.c_void_p((1 << 20) + 2), 10, fake, None) == moe.MOE_ERR_INVALID
+    assert L.moe_check_pow2_scales(None, 0, fake, None) == moe.MOE_OK
 
 
 def test_dispatch_rejects():

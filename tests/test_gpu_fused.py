@@ -4,7 +4,8 @@ recv_src, flags, FP8 codes and scales or BF16 copies -- bit-identical to the
 oracle's route -> layout -> dispatch, for decode-sized batches, ragged shapes,
 every routing path (grouped, general groups, no groups, softmax), padded,
 compact and aligned layouts, all three dispatch dtypes, and repeated calls
-on one barrier workspace."""
+on one barrier workspace; a workspace marked as given up (set from the
+host, so no block ever waits) is refused and reported in flags."""
 import sys
 
 import numpy as np
@@ -191,3 +192,24 @@ def test_route_dispatch_rejects_large_batches():
         moe.route_dispatch(torch.zeros((wl.T, wl.E), dtype=torch.float32, device=DEV),
                            torch.zeros((wl.T, wl.H), dtype=torch.bfloat16, device=DEV), wl.G, wl.g, wl.k, wl.R)
     assert e.value.status == moe.MOE_ERR_UNSUPPORTED
+
+
+def test_route_dispatch_refused_workspace():
+    """A workspace whose give-up word is nonzero (set here from the host: no
+    block is ever made to wait) is refused: the call reports
+    MOE_FLAG_INCOMPLETE and leaves the barrier words as they were; zeroed
+    again, the workspace works."""
+    wl = W.get("ll_decode")
+    say("[gpu] route_dispatch on a refused workspace")
+    ws = moe.route_dispatch_workspace(DEV)
+    ws.view(torch.int32)[2] = 1
+    before = ws.clone()
+    out = prefilled_out(wl, wl.N, "fp8")
+    _, _, lay, _, _ = moe.route_dispatch(torch.from_numpy(W.gen_logits(wl)).to(DEV), bf16_to_dev(W.gen_x(wl)),
+                                         wl.G, wl.g, wl.k, wl.R, wl.capacity, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    assert int(lay.flags.item()) == moe.FLAG_INCOMPLETE
+    assert torch.equal(ws, before)
+    assert moe.barrier_gave_up(ws) == 1
+    moe.reset_barrier_workspace(ws)
+    run_case(wl, ws=ws)

@@ -11,7 +11,8 @@ separate calls: every array bit for bit, with different sentinels in the two
 sets of buffers so that a row neither path writes cannot pass unseen.  Both
 also check compact, tile-aligned and padded layouts, 256-row and 128-row
 expert tiles, and several calls in a row on one barrier workspace, which must
-be left at rest."""
+be left at rest; a workspace marked as given up (from the host: no block is
+ever made to wait) is refused without touching the barrier's words."""
 import sys
 
 import numpy as np
@@ -251,3 +252,39 @@ def test_layer_graph_replays():
         words = ws.view(torch.int32).cpu().numpy()
         assert words[0] == 0 and words[2] == 0, words[:3]
         say(f"   replay {rep} (seed {seed}) identical to an eager call")
+
+
+def test_layer_refused_workspace():
+    """Give-up word set from the host: the launch stops at its first barrier
+    without arriving (barrier words unchanged) and barrier_gave_up reports it;
+    after reset_barrier_workspace the same call equals the four calls."""
+    T, H, I, E, G, g, k, R = 300, 1024, 384, 32, 8, 4, 8, 8
+    say("[gpu] one-launch layer on a refused workspace")
+    wl = W.custom("layer_ref", T=T, H=H, E=E, G=G, g=g, k=k, score="sigmoid", R=R, dtype="fp8")
+    mw = W.MlpWorkload("layer_ref_mlp", N=1, H=H, I=I, E=E, seed=7)
+    d = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+    w1, w1s = map(d, W.gen_mlp_weights(mw, "w1"))
+    w2, w2s = map(d, W.gen_mlp_weights(mw, "w2"))
+    x = bf16_to_dev(W.gen_x(wl))
+    idx, w = moe.route_topk(d(W.gen_logits(wl)), G, g, k)
+    lay = moe.get_layout(idx, E, R)
+    N = lay.num_recv_rows
+    ws = moe.layer_workspace(DEV)
+    ws.view(torch.int32)[2] = 3
+    before = ws.view(torch.int32)[:768].clone()
+    moe.layer_forward(x, lay.pos, w, lay.cnt_e, lay.off_e, w1, w1s, w2, w2s, N, workspace=ws,
+                      buffers=fresh(N, H, I, 0))
+    torch.cuda.synchronize()
+    assert torch.equal(ws.view(torch.int32)[:768], before)
+    assert moe.barrier_gave_up(ws) == 3
+    moe.reset_barrier_workspace(ws)
+    out1, b1 = moe.layer_forward(x, lay.pos, w, lay.cnt_e, lay.off_e, w1, w1s, w2, w2s, N, workspace=ws,
+                                 buffers=fresh(N, H, I, 0))
+    rx, rs, act, act_s, y = fresh(N, H, I, 1)
+    moe.dispatch(x, lay.pos, N, "fp8_pow2", rx, rs)
+    moe.expert_up(rx, rs, w1, w1s, lay.cnt_e, lay.off_e, 0, act, act_s)
+    moe.expert_down(act, act_s, w2, w2s, lay.cnt_e, lay.off_e, 0, y)
+    out = moe.combine(y, lay.pos, w)
+    torch.cuda.synchronize()
+    assert same(out, out1) and same(y, b1[4])
+    assert moe.barrier_gave_up(ws) == 0

@@ -179,3 +179,16 @@ def test_mlp_unaligned_scales_match_aligned(N, H, I, E):
 def test_mlp_zero_rows_is_noop():
     cfg = moe.MlpCfg(0, 7168, 2048, 8, 0)
     assert moe.lib().moe_expert_up(cfg, None, None, None, None, None, None, None, None, None) == moe.MOE_OK
+
+
+def test_check_pow2_scales():
+    """The precondition check flags exactly the scales that are not positive
+    normal powers of two."""
+    good = torch.tensor([2.0 ** e for e in range(-126, 128)], dtype=torch.float32, device=DEV)
+    assert moe.check_pow2_scales(good)
+    big = torch.full((5000,), 0.25, dtype=torch.float32, device=DEV)
+    assert moe.check_pow2_scales(good, big)
+    for bad in (3.0, -2.0, 0.0, -0.0, 2.0 ** -127, float("inf"), float("nan"), 1.5 * 2 ** -20):
+        b = big.clone()
+        b[4321] = bad
+        assert not moe.check_pow2_scales(good, b), bad
