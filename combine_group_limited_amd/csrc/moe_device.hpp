@@ -300,6 +300,17 @@ __device__ __forceinline__ u32x2 quantize_unit(const u32x4& v, float& scale) {
     return code;
 }
 
+// Sum over the wave (DPP inside rows of 16, the four row sums on the scalar
+// unit), returned in every lane.
+__device__ __forceinline__ int wave_sum(int v) {
+    v += (int)dpp32<0xB1>((uint32_t)v);
+    v += (int)dpp32<0x4E>((uint32_t)v);
+    v += (int)dpp32<0x141>((uint32_t)v);
+    v += (int)dpp32<0x140>((uint32_t)v);
+    return __builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16) + __builtin_amdgcn_readlane(v, 32) +
+           __builtin_amdgcn_readlane(v, 48);
+}
+
 // Inclusive scan of one value per lane across a wave.
 __device__ __forceinline__ int wave_inclusive_scan(int v) {
     const int lane = threadIdx.x & 63;
