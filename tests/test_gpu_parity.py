@@ -247,6 +247,34 @@ def test_route_group_topn_override():
         assert np.array_equal(w.cpu().numpy(), ref_w), n
 
 
+# The row-routing kernel (four tokens per wave) serves batches of 2048 tokens
+# or more with E in {16, 32, 64, 128, 256}, G dividing 16 and k <= 16; every
+# such shape family, both score functions and both weightings, ragged token
+# counts and tie-heavy logits, bit for bit against the oracle.
+@pytest.mark.parametrize("T,E,G,g,k,n", [
+    (2048, 16, 4, 2, 3, 0), (2053, 32, 2, 1, 5, 0), (2100, 64, 16, 4, 16, 0), (4099, 128, 8, 3, 7, 0),
+    (2048, 256, 1, 1, 8, 0), (3001, 256, 16, 8, 12, 0), (2050, 256, 8, 4, 8, 3), (2047, 256, 8, 4, 8, 0),
+])
+@pytest.mark.parametrize("tie", [False, True])
+def test_route_rows_shapes(T, E, G, g, k, n, tie):
+    wl = W.custom("rows", T=T, H=128, E=E, G=G, g=g, k=k, score="sigmoid", R=1, dtype="fp8", seed=T + E)
+    say(f"[gpu] route rows T={T} E={E} G={G} g={g} k={k} n={n} tie={tie}")
+    logits = W.gen_logits(wl)
+    if tie:
+        logits = W.tie_heavy(logits)
+        logits[0, :] = 0.0
+        logits[1, ::2] = -0.0
+        logits[2, :] = -100.0
+        logits[3, :] = 100.0
+    for score in ("sigmoid", "softmax"):
+        for renorm in (True, False):
+            ref_i, ref_w = oracle.route(logits, G, g, k, score_fn=oracle.SIGMOID if score == "sigmoid"
+                                        else oracle.SOFTMAX, renormalize=renorm, group_topn=n)
+            idx, w = moe.route_topk(torch.from_numpy(logits).to(DEV), G, g, k, score, renorm, group_topn=n)
+            assert np.array_equal(idx.cpu().numpy(), ref_i), (score, renorm)
+            assert np.array_equal(w.cpu().numpy().view(np.uint32), ref_w.view(np.uint32)), (score, renorm)
+
+
 def test_dispatch_adversarial_rows():
     wl = W.custom("adv", T=64, H=1024, E=16, G=4, g=2, k=2, score="sigmoid", R=4, dtype="fp8")
     say("[gpu] adversarial dispatch rows")
@@ -297,6 +325,28 @@ def test_layout_flags_bad_indices():
     idx[-1, 1] = 4
     lay = moe.get_layout(torch.from_numpy(idx).to(DEV), 4, 2)
     assert int(lay.flags.item()) == moe.FLAG_BAD_INDEX
+
+
+def random_idx(T, E, k, seed):
+    """k distinct experts per token: the first k of a seeded random order."""
+    return np.argsort(np.random.default_rng(seed).random((T, E)), axis=1)[:, :k].astype(np.int32)
+
+
+@pytest.mark.parametrize("T,E,k,R,C", [
+    (1, 256, 8, 32, 0), (1023, 256, 8, 32, 0), (1025, 64, 4, 8, 0), (32768, 16, 2, 4, 0),
+    (32769, 16, 2, 4, 0),          # above the one-launch limit: the two-launch path
+    (32768, 512, 3, 8, 0),         # general k, the most tokens and experts of the one launch
+    (5000, 256, 8, 32, 20),        # padded, overflowing experts
+    (32768, 64, 1, 64, 600),       # padded at the one-launch limit, k = 1
+])
+def test_layout_token_limits(T, E, k, R, C):
+    say(f"[gpu] layout T={T} E={E} k={k} R={R} C={C}")
+    idx = random_idx(T, E, k, T + E)
+    ref = oracle.layout(idx, E, R, C)
+    lay = moe.get_layout(torch.from_numpy(idx).to(DEV), E, R, C)
+    for name in ("cnt_e", "cnt_r", "off_e", "off_r", "pos", "recv_src"):
+        assert np.array_equal(getattr(lay, name).cpu().numpy(), ref[name]), name
+    assert int(lay.flags.item()) == ref["flags"]
 
 
 def test_layout_capacity_overflow_multiblock():
@@ -411,3 +461,28 @@ def test_dispatch_pow2_parity(name):
                         torch.zeros((wl.N, wl.S), dtype=torch.float32, device=DEV))
     assert np.array_equal(q.cpu().numpy(), ref_q)
     assert np.array_equal(s.cpu().numpy().view(np.uint32), ref_s.view(np.uint32))
+
+
+@pytest.mark.parametrize("name", ["dsv3_prefill", "tiny", "ll_decode", "skewed_8k"])
+def test_dispatch_ue8m0_parity(name):
+    """One-byte E8M0 scales: codes and scale bytes bit-exact, rows no pair
+    addresses (padded layout) untouched, at the full shapes in the library's
+    launch configuration."""
+    wl = W.get(name)
+    say(f"[gpu] ue8m0 dispatch {name}")
+    x = W.gen_x(wl)
+    x[0] = 0
+    x[1, :128] = W.f32_to_bf16_bits(np.full(128, 448.0, np.float32))
+    x[2, :128] = W.f32_to_bf16_bits(np.full(128, 450.0, np.float32))
+    x[3] = W.f32_to_bf16_bits(W.bf16_bits_to_f32(x[3]) * np.float32(3e38 / 5))
+    x[4] = W.f32_to_bf16_bits(W.bf16_bits_to_f32(x[4]) * np.float32(1e-38))
+    idx, _ = oracle.route(W.gen_logits(wl), wl.G, wl.g, wl.k)
+    lay = oracle.layout(idx, wl.E, wl.R, wl.capacity)
+    ref_q, ref_s = oracle.dispatch(x, lay["pos"], wl.N, oracle.FP8_UE8M0,
+                                   np.full((wl.N, wl.H), 0xCD, np.uint8), np.full((wl.N, wl.S), 0xEE, np.uint8))
+    q, s = moe.dispatch(bf16_to_dev(x), torch.from_numpy(lay["pos"]).to(DEV), wl.N, "fp8_ue8m0",
+                        torch.full((wl.N, wl.H), 0xCD, dtype=torch.uint8, device=DEV),
+                        torch.full((wl.N, wl.S), 0xEE, dtype=torch.uint8, device=DEV))
+    assert s.dtype == torch.uint8
+    assert np.array_equal(q.cpu().numpy(), ref_q)
+    assert np.array_equal(s.cpu().numpy(), ref_s)
