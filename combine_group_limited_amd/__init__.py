@@ -21,7 +21,8 @@ LIB_PATH = os.path.join(PKG, "libcgl_moe.so")
 
 MOE_OK, MOE_ERR_INVALID, MOE_ERR_WORKSPACE, MOE_ERR_UNSUPPORTED, MOE_ERR_HIP = 0, 1, 2, 4, 5
 SCORE_FNS = {"sigmoid": 0, "softmax": 1}
-DISPATCH_DTYPES = {"fp8": 0, "bf16": 1, "fp8_pow2": 2}
+DISPATCH_DTYPES = {"fp8": 0, "bf16": 1, "fp8_pow2": 2, "fp8_ue8m0": 3}
+FP8_DTYPES = ("fp8", "fp8_pow2", "fp8_ue8m0")
 FLAG_CAPACITY_OVERFLOW, FLAG_BAD_INDEX, FLAG_INCOMPLETE, FLAG_BAD_SCALE = 1, 2, 4, 8
 
 
@@ -238,7 +239,8 @@ def get_layout_noalloc(topk_idx, num_experts: int, num_ranks: int, layout: Layou
 
 def dispatch(x, pos, num_recv_rows: int, dtype: str = "fp8", recv_x=None, recv_scales=None,
              units_per_wave: int = 0):
-    """x bf16 [T,H] -> (recv_x uint8 [N,H] or bf16 [N,H], recv_scales fp32 [N,H/128] or None)."""
+    """x bf16 [T,H] -> (recv_x uint8 [N,H] or bf16 [N,H], recv_scales [N,H/128] or None):
+    fp32 scales for "fp8" and "fp8_pow2", uint8 E8M0 exponent bytes for "fp8_ue8m0"."""
     torch = _torch()
     _need(x, "x", torch.bfloat16)
     _need(pos, "pos", torch.int32, device=x.device)
@@ -246,16 +248,17 @@ def dispatch(x, pos, num_recv_rows: int, dtype: str = "fp8", recv_x=None, recv_s
     k = pos.shape[1]
     if pos.shape[0] != T:
         raise ValueError("pos must be [T, k]")
-    fp8 = dtype in ("fp8", "fp8_pow2")
+    fp8 = dtype in FP8_DTYPES
+    sdt = torch.uint8 if dtype == "fp8_ue8m0" else torch.float32
     if recv_x is None:
         recv_x = torch.empty((num_recv_rows, H), dtype=torch.uint8 if fp8 else torch.bfloat16,
                              device=x.device)
     else:
         _need(recv_x, "recv_x", torch.uint8 if fp8 else torch.bfloat16, (num_recv_rows, H), x.device)
     if fp8 and recv_scales is None:
-        recv_scales = torch.empty((num_recv_rows, H // 128), dtype=torch.float32, device=x.device)
+        recv_scales = torch.empty((num_recv_rows, H // 128), dtype=sdt, device=x.device)
     elif fp8:
-        _need(recv_scales, "recv_scales", torch.float32, (num_recv_rows, H // 128), x.device)
+        _need(recv_scales, "recv_scales", sdt, (num_recv_rows, H // 128), x.device)
     cfg = DispatchCfg(T, H, k, num_recv_rows, DISPATCH_DTYPES[dtype], units_per_wave)
     _check(lib().moe_dispatch(ctypes.byref(cfg), _ptr(x), _ptr(pos), _ptr(recv_x),
                               _ptr(recv_scales) if fp8 else None, _stream(x.device)))
@@ -292,20 +295,21 @@ def route_dispatch(logits, x, num_groups: int, topk_group: int, topk: int, num_r
         raise ValueError("x must be [T, H] with the T of logits")
     dev = logits.device
     N = recv_rows(T, E, topk, capacity, align_rows)
-    fp8 = dtype in ("fp8", "fp8_pow2")
+    fp8 = dtype in FP8_DTYPES
+    sdt = torch.uint8 if dtype == "fp8_ue8m0" else torch.float32
     if out is None:
         idx = torch.empty((T, topk), dtype=torch.int32, device=dev)
         w = torch.empty((T, topk), dtype=torch.float32, device=dev)
         lay = alloc_layout(T, E, topk, num_ranks, capacity, dev, align_rows)[0]
         recv_x = torch.empty((N, H), dtype=torch.uint8 if fp8 else torch.bfloat16, device=dev)
-        recv_scales = torch.empty((N, H // 128), dtype=torch.float32, device=dev) if fp8 else None
+        recv_scales = torch.empty((N, H // 128), dtype=sdt, device=dev) if fp8 else None
     else:
         idx, w, lay, recv_x, recv_scales = out
         _need(idx, "idx", torch.int32, (T, topk), dev)
         _need(w, "w", torch.float32, (T, topk), dev)
         _need(recv_x, "recv_x", torch.uint8 if fp8 else torch.bfloat16, (N, H), dev)
         if fp8:
-            _need(recv_scales, "recv_scales", torch.float32, (N, H // 128), dev)
+            _need(recv_scales, "recv_scales", sdt, (N, H // 128), dev)
         if lay.num_recv_rows != N:
             raise ValueError("layout buffers were sized for another receive layout")
     if workspace is None:

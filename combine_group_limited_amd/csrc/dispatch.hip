@@ -22,9 +22,9 @@
 namespace cgl {
 namespace {
 
-template <int U, bool POW2>
+template <int U, int MODE>
 __global__ __launch_bounds__(kDispatchThreads) void dispatch_fp8_kernel(DispatchArgs a) {
-    dispatch_fp8_wave<U, POW2>(a, blockIdx.x * (kDispatchThreads / kWave) + wave_in_block());
+    dispatch_fp8_wave<U, MODE>(a, blockIdx.x * (kDispatchThreads / kWave) + wave_in_block());
 }
 
 template <int U>
@@ -40,13 +40,13 @@ hipError_t launch_u(DispatchArgs a, int dtype, hipStream_t s) {
     const int wpb = kDispatchThreads / kWave;
     const unsigned blocks = (unsigned)((waves + wpb - 1) / wpb);
     if (dtype == 0)
-        hipLaunchKernelGGL((dispatch_fp8_kernel<U, false>), dim3(blocks), dim3(kDispatchThreads), CGL_DISPATCH_LDS_CAP,
-                           s, a);
+        hipLaunchKernelGGL((dispatch_fp8_kernel<U, kScaleF32>), dim3(blocks), dim3(kDispatchThreads), 0, s, a);
     else if (dtype == 2)
-        hipLaunchKernelGGL((dispatch_fp8_kernel<U, true>), dim3(blocks), dim3(kDispatchThreads), CGL_DISPATCH_LDS_CAP,
-                           s, a);
+        hipLaunchKernelGGL((dispatch_fp8_kernel<U, kScalePow2>), dim3(blocks), dim3(kDispatchThreads), 0, s, a);
+    else if (dtype == 3)
+        hipLaunchKernelGGL((dispatch_fp8_kernel<U, kScaleUE8M0>), dim3(blocks), dim3(kDispatchThreads), 0, s, a);
     else
-        hipLaunchKernelGGL((dispatch_bf16_kernel<U>), dim3(blocks), dim3(kDispatchThreads), CGL_DISPATCH_LDS_CAP, s, a);
+        hipLaunchKernelGGL((dispatch_bf16_kernel<U>), dim3(blocks), dim3(kDispatchThreads), 0, s, a);
     return hipGetLastError();
 }
 
@@ -64,7 +64,7 @@ int dispatch_units_per_wave(int T, int H) {
     return 1;
 }
 
-hipError_t launch_dispatch(const uint16_t* x, const int32_t* pos, void* recv_x, float* recv_scales, int T,
+hipError_t launch_dispatch(const uint16_t* x, const int32_t* pos, void* recv_x, void* recv_scales, int T,
                            int H, int k, int N, int dtype, int upw, hipStream_t stream) {
     DispatchArgs a{};
     a.x = x;

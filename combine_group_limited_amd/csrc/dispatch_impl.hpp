@@ -9,40 +9,26 @@ namespace cgl {
 namespace {
 
 constexpr int kDispatchUnit = 512;             // channels per wave-wide 16-byte load
-#ifndef CGL_DISPATCH_THREADS
-#define CGL_DISPATCH_THREADS 256
-#endif
-// LDS bytes requested per block only to cap how many blocks share a CU
-// (0 = no cap)
-#ifndef CGL_DISPATCH_LDS_CAP
-#define CGL_DISPATCH_LDS_CAP 0
-#endif
-constexpr int kDispatchThreads = CGL_DISPATCH_THREADS;  // waves per block = threads / 64
+constexpr int kDispatchThreads = 256;          // waves per block = threads / 64
 constexpr long long kDrainWaves = 2048;
 
-// cache policy of the x reads and the receive-buffer writes (1 = streaming).
+// Cache policy of the x reads and the receive-buffer writes (1 = streaming).
 // Measured on MI355X at 4096 x 7168 top-8: streaming loads with ordinary
-// stores are fastest in the dispatch -> combine sequence.
-#ifndef CGL_DISPATCH_LOAD_NT
-#define CGL_DISPATCH_LOAD_NT 1
-#endif
-#ifndef CGL_DISPATCH_STORE_NT
-#define CGL_DISPATCH_STORE_NT 0
-#endif
-// 1: wait until a destination row's stores have completed before starting
-// the next row (fewer rows open at once across the chip) when the grid has
-// at least kDrainWaves waves; smaller grids leave every row in flight.
-// Measured on MI355X: 48.9 vs 52.6 us at 4096 tokens (4 096 waves), but
-// 4.6 vs 3.8 us at 128 tokens (1 792 waves).
-#ifndef CGL_DISPATCH_DRAIN
-#define CGL_DISPATCH_DRAIN 1
-#endif
+// stores are fastest in the dispatch -> combine sequence (48 us against
+// 57-59 us with streaming stores).
+constexpr int kDispatchLoadNT = 1;
+constexpr int kDispatchStoreNT = 0;
+// Grids of at least kDrainWaves waves wait until a destination row's stores
+// have completed before starting the next row (fewer rows open at once across
+// the chip); smaller grids leave every row in flight.  Measured on MI355X:
+// 48.9 vs 52.6 us at 4096 tokens (4 096 waves), but 4.6 vs 3.8 us at 128
+// tokens (1 792 waves).
 
 struct DispatchArgs {
     const uint16_t* x;
     const int32_t* pos;
     void* recv_x;
-    float* recv_scales;
+    void* recv_scales;  // fp32 [N, S], or uint8 [N, S] E8M0 exponent bytes
     int T, H, k, N, S;
     int units;   // ceil(H / 512)
     int chunks;  // ceil(units / U): waves per token
@@ -50,10 +36,26 @@ struct DispatchArgs {
 };
 
 __device__ __forceinline__ u32x4 load16(const uint16_t* p) {
-    return load_stream<CGL_DISPATCH_LOAD_NT>((const u32x4*)p);
+    return load_stream<kDispatchLoadNT>((const u32x4*)p);
 }
 
-template <int U, bool POW2>
+// Scale formats of the FP8 dispatch: amax/448 in fp32, a power of two in
+// fp32, or the same power of two as one E8M0 byte (its biased exponent).
+enum { kScaleF32 = 0, kScalePow2 = 2, kScaleUE8M0 = 3 };
+
+__device__ __forceinline__ uint8_t e8m0_byte(float pow2_scale) {
+    return (uint8_t)((__float_as_uint(pow2_scale) >> 23) & 0xFFu);
+}
+
+template <int MODE>
+__device__ __forceinline__ void store_scale(void* scales, size_t i, float scale) {
+    if constexpr (MODE == kScaleUE8M0)
+        ((uint8_t*)scales)[i] = e8m0_byte(scale);
+    else
+        ((float*)scales)[i] = scale;
+}
+
+template <int U, int MODE>
 __device__ __forceinline__ void dispatch_fp8_wave(const DispatchArgs& a, int wave) {
     const int lane = threadIdx.x & 63;
     const int t = wave / a.chunks;
@@ -76,7 +78,7 @@ __device__ __forceinline__ void dispatch_fp8_wave(const DispatchArgs& a, int wav
     float scale[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        code[u] = quantize_unit<POW2>(v[u], scale[u]);
+        code[u] = quantize_unit<MODE != kScaleF32>(v[u], scale[u]);
     }
 
     uint8_t* rx = (uint8_t*)a.recv_x;
@@ -84,16 +86,15 @@ __device__ __forceinline__ void dispatch_fp8_wave(const DispatchArgs& a, int wav
         const int p = __builtin_amdgcn_readlane(pv, j);
         if (p < 0 || p >= a.N) continue;  // dropped pair (wave-uniform)
         uint8_t* dst = rx + (size_t)p * a.H;
-        float* sdst = a.recv_scales + (size_t)p * a.S;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int c = (u0 + u) * kDispatchUnit + lane * 8;
             if (c < a.H) {
-                store_stream<CGL_DISPATCH_STORE_NT>(code[u], (u32x2*)(dst + c));
-                if ((lane & 15) == 0) sdst[c >> 7] = scale[u];
+                store_stream<kDispatchStoreNT>(code[u], (u32x2*)(dst + c));
+                if ((lane & 15) == 0) store_scale<MODE>(a.recv_scales, (size_t)p * a.S + (c >> 7), scale[u]);
             }
         }
-        if (CGL_DISPATCH_DRAIN && a.drain) __builtin_amdgcn_s_waitcnt(kWaitStores);
+        if (a.drain) __builtin_amdgcn_s_waitcnt(kWaitStores);
     }
 }
 
@@ -119,9 +120,9 @@ __device__ __forceinline__ void dispatch_bf16_wave(const DispatchArgs& a, int wa
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int c = (u0 + u) * kDispatchUnit + lane * 8;
-            if (c < a.H) store_stream<CGL_DISPATCH_STORE_NT>(v[u], (u32x4*)(dst + c));
+            if (c < a.H) store_stream<kDispatchStoreNT>(v[u], (u32x4*)(dst + c));
         }
-        if (CGL_DISPATCH_DRAIN && a.drain) __builtin_amdgcn_s_waitcnt(kWaitStores);
+        if (a.drain) __builtin_amdgcn_s_waitcnt(kWaitStores);
     }
 }
 

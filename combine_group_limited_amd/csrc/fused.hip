@@ -31,6 +31,7 @@
 // block arrives.  Device-scope release/acquire fences would instead write back
 // and invalidate each XCD's whole L2 once per block: measured on MI355X at
 // 128 tokens, they cost 11 us of a 17 us launch.
+#include "dispatch_impl.hpp"
 #include "grid_barrier.hpp"
 #include "moe_internal.hpp"
 #include "route_impl.hpp"
@@ -49,7 +50,7 @@ struct FusedArgs {
     int32_t *cnt_e, *cnt_r, *off_e, *off_r, *pos, *recv_src, *flags;
     const uint16_t* x;
     void* recv_x;
-    float* recv_scales;
+    void* recv_scales;
     uint32_t* bar;  // barrier workspace (see grid_barrier); word 2: blocks that gave up
     int R, C, A, N;
     int H, S, units, dtype;
@@ -80,14 +81,19 @@ __device__ __forceinline__ void store_unit(const FusedArgs& a, const int32_t* po
                 *(u32x4*)((uint16_t*)a.recv_x + (size_t)p * a.H + c) = v;
             } else {
                 *(u32x2*)((uint8_t*)a.recv_x + (size_t)p * a.H + c) = code;
-                if ((lane & 15) == 0) a.recv_scales[(size_t)p * a.S + (c >> 7)] = scale;
+                if ((lane & 15) == 0) {
+                    if (a.dtype == 3)
+                        store_scale<kScaleUE8M0>(a.recv_scales, (size_t)p * a.S + (c >> 7), scale);
+                    else
+                        store_scale<kScaleF32>(a.recv_scales, (size_t)p * a.S + (c >> 7), scale);
+                }
             }
         }
     }
 }
 
 __device__ __forceinline__ u32x2 quantize(const FusedArgs& a, const u32x4& v, float& scale) {
-    if (a.dtype == 2) return quantize_unit<true>(v, scale);
+    if (a.dtype >= 2) return quantize_unit<true>(v, scale);
     return quantize_unit<false>(v, scale);  // also run for BF16, result unused
 }
 
@@ -253,7 +259,7 @@ size_t fused_decode_lds_bytes(int T, int E, int k, int R) { return fused_lds_byt
 
 hipError_t launch_fused_decode(const float* logits, const uint16_t* x, int32_t* idx, float* w, int32_t* cnt_e,
                                int32_t* cnt_r, int32_t* off_e, int32_t* off_r, int32_t* pos, int32_t* recv_src,
-                               int32_t* flags, void* recv_x, float* recv_scales, uint32_t* barrier, int T, int E,
+                               int32_t* flags, void* recv_x, void* recv_scales, uint32_t* barrier, int T, int E,
                                int G, int g, int k, int n, int score_fn, int renorm, int R, int C, int A, int N,
                                int H, int dtype, hipStream_t stream) {
     FusedArgs a{};

@@ -77,12 +77,12 @@ __device__ __forceinline__ void layer_dispatch(const DispatchArgs& a, int w0, in
             const int p = __builtin_amdgcn_readlane(pv, j);
             if (p < 0 || p >= a.N) continue;  // dropped pair (wave-uniform)
             uint8_t* dst = rx + (size_t)p * a.H;
-            float* sdst = a.recv_scales + (size_t)p * a.S;
+            float* sdst = (float*)a.recv_scales + (size_t)p * a.S;
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int c = (u0 + u) * kDispatchUnit + lane * 8;
                 if (c < a.H) {
-                    store_stream<CGL_DISPATCH_STORE_NT>(code[u], (u32x2*)(dst + c));
+                    store_stream<kDispatchStoreNT>(code[u], (u32x2*)(dst + c));
                     if ((lane & 15) == 0) sdst[c >> 7] = scale[u];
                 }
             }
@@ -153,7 +153,7 @@ __device__ __forceinline__ void layer_combine(const CombineArgs& a, int w0, int 
                 o.y = pack_bf16x2(acc[u][2], acc[u][3]);
                 o.z = pack_bf16x2(acc[u][4], acc[u][5]);
                 o.w = pack_bf16x2(acc[u][6], acc[u][7]);
-                store_stream<CGL_COMBINE_STORE_NT>(o, (u32x4*)(orow + c));
+                store_stream<kCombineStoreNT>(o, (u32x4*)(orow + c));
             }
         }
     }

@@ -88,7 +88,7 @@ using namespace cgl;
 
 extern "C" {
 
-int32_t moe_abi_version(void) { return 7; }
+int32_t moe_abi_version(void) { return 8; }
 
 const char* moe_last_error(void) { return g_err; }
 
@@ -229,7 +229,8 @@ static moe_status check_dispatch_cfg(const moe_dispatch_cfg* c) {
     const int T = c->num_tokens, H = c->hidden, k = c->topk, N = c->num_recv_rows;
     if (T < 0 || N < 0) return fail(MOE_ERR_INVALID, "dispatch: negative size");
     if (k < 1 || k > 64) return fail(MOE_ERR_INVALID, "dispatch: topk %d outside [1, 64]", k);
-    const bool fp8 = c->dtype == MOE_DISPATCH_FP8_E4M3 || c->dtype == MOE_DISPATCH_FP8_E4M3_POW2;
+    const bool fp8 = c->dtype == MOE_DISPATCH_FP8_E4M3 || c->dtype == MOE_DISPATCH_FP8_E4M3_POW2 ||
+                     c->dtype == MOE_DISPATCH_FP8_E4M3_UE8M0;
     if (!fp8 && c->dtype != MOE_DISPATCH_BF16) return fail(MOE_ERR_INVALID, "dispatch: unknown dtype %d", c->dtype);
     if (H < 1 || (fp8 && H % 128) || (!fp8 && H % 8))
         return fail(MOE_ERR_INVALID, "dispatch: hidden %d must be a positive multiple of %d", H, fp8 ? 128 : 8);
@@ -240,7 +241,7 @@ static moe_status check_dispatch_cfg(const moe_dispatch_cfg* c) {
 }
 
 moe_status moe_dispatch(const moe_dispatch_cfg* c, const uint16_t* x, const int32_t* pos, void* recv_x,
-                        float* recv_scales, void* stream) {
+                        void* recv_scales, void* stream) {
     const moe_status st = check_dispatch_cfg(c);
     if (st != MOE_OK) return st;
     const int T = c->num_tokens, H = c->hidden, k = c->topk, N = c->num_recv_rows;
@@ -248,8 +249,9 @@ moe_status moe_dispatch(const moe_dispatch_cfg* c, const uint16_t* x, const int3
     if (T == 0) return ok();
     if (!x || !pos || (N > 0 && !recv_x) || (fp8 && N > 0 && !recv_scales))
         return fail(MOE_ERR_INVALID, "dispatch: NULL array");
-    if (!aligned(x, 16) || !aligned(recv_x, 16) || !aligned(pos, 4) || !aligned(recv_scales, 4))
-        return fail(MOE_ERR_INVALID, "dispatch: x/recv_x must be 16-byte aligned, pos/scales 4-byte");
+    const size_t sc_align = c->dtype == MOE_DISPATCH_FP8_E4M3_UE8M0 ? 1 : 4;
+    if (!aligned(x, 16) || !aligned(recv_x, 16) || !aligned(pos, 4) || !aligned(recv_scales, sc_align))
+        return fail(MOE_ERR_INVALID, "dispatch: x/recv_x must be 16-byte aligned, pos and fp32 scales 4-byte");
     if (N == 0) return ok();
     return hip_status(launch_dispatch(x, pos, recv_x, recv_scales, T, H, k, N, c->dtype, c->units_per_wave,
                                       (hipStream_t)stream),
@@ -261,7 +263,7 @@ size_t moe_route_dispatch_workspace_bytes(void) { return 4096; }
 moe_status moe_route_dispatch(const moe_route_cfg* rc, const moe_layout_cfg* lc, const moe_dispatch_cfg* dc,
                               const float* logits, const uint16_t* x, int32_t* topk_idx, float* topk_w,
                               int32_t* cnt_e, int32_t* cnt_r, int32_t* off_e, int32_t* off_r, int32_t* pos,
-                              int32_t* recv_src, int32_t* flags, void* recv_x, float* recv_scales, void* workspace,
+                              int32_t* recv_src, int32_t* flags, void* recv_x, void* recv_scales, void* workspace,
                               size_t workspace_bytes, void* stream) {
     int n = 0;
     moe_status st = check_route_cfg(rc, &n);
@@ -292,7 +294,8 @@ moe_status moe_route_dispatch(const moe_route_cfg* rc, const moe_layout_cfg* lc,
         return fail(MOE_ERR_INVALID, "route_dispatch: NULL array");
     if (N > 0 && (!recv_src || !recv_x || (fp8 && !recv_scales)))
         return fail(MOE_ERR_INVALID, "route_dispatch: NULL receive array");
-    const void* p4[] = {logits, topk_idx, topk_w, cnt_e, cnt_r, off_e, off_r, pos, recv_src, flags, recv_scales};
+    const void* p4[] = {logits, topk_idx, topk_w, cnt_e, cnt_r, off_e, off_r, pos, recv_src, flags,
+                        dc->dtype == MOE_DISPATCH_FP8_E4M3_UE8M0 ? nullptr : recv_scales};
     for (const void* p : p4)
         if (!aligned(p, 4)) return fail(MOE_ERR_INVALID, "route_dispatch: arrays must be 4-byte aligned");
     if (!aligned(x, 16) || !aligned(recv_x, 16))

@@ -22,8 +22,9 @@ hipError_t launch_layout(const int32_t* idx, int32_t* cnt_e, int32_t* cnt_r, int
 
 // upw: 512-channel units per wave (0 = the library's choice for the shape)
 int dispatch_units_per_wave(int T, int H);
-// dtype: 0 FP8 (amax/448 scales), 1 BF16, 2 FP8 with power-of-two scales
-hipError_t launch_dispatch(const uint16_t* x, const int32_t* pos, void* recv_x, float* recv_scales, int T,
+// dtype: 0 FP8 (amax/448 scales), 1 BF16, 2 FP8 with power-of-two scales, 3 the same
+// with one E8M0 exponent byte per scale
+hipError_t launch_dispatch(const uint16_t* x, const int32_t* pos, void* recv_x, void* recv_scales, int T,
                            int H, int k, int N, int dtype, int upw, hipStream_t stream);
 
 int combine_units_per_wave(int T, int H);
@@ -40,7 +41,7 @@ constexpr size_t kFusedMaxLds = 64512;  // 64 KiB of dynamic LDS less 1 KiB for 
 size_t fused_decode_lds_bytes(int T, int E, int k, int R);
 hipError_t launch_fused_decode(const float* logits, const uint16_t* x, int32_t* idx, float* w, int32_t* cnt_e,
                                int32_t* cnt_r, int32_t* off_e, int32_t* off_r, int32_t* pos, int32_t* recv_src,
-                               int32_t* flags, void* recv_x, float* recv_scales, uint32_t* barrier, int T, int E,
+                               int32_t* flags, void* recv_x, void* recv_scales, uint32_t* barrier, int T, int E,
                                int G, int g, int k, int n, int score_fn, int renorm, int R, int C, int A, int N,
                                int H, int dtype, hipStream_t stream);
 

@@ -56,7 +56,8 @@ typedef enum { MOE_SCORE_SIGMOID = 0, MOE_SCORE_SOFTMAX = 1 } moe_score_fn;
 typedef enum {
     MOE_DISPATCH_FP8_E4M3 = 0,      /* fp32 scale = amax / 448 per 128 channels */
     MOE_DISPATCH_BF16 = 1,          /* verbatim copy */
-    MOE_DISPATCH_FP8_E4M3_POW2 = 2  /* power-of-two scale per 128 channels */
+    MOE_DISPATCH_FP8_E4M3_POW2 = 2, /* power-of-two scale per 128 channels */
+    MOE_DISPATCH_FP8_E4M3_UE8M0 = 3 /* the same scale as one E8M0 byte */
 } moe_dispatch_dtype;
 
 /* Bits of the *flags word written by moe_get_layout. */
@@ -204,13 +205,19 @@ moe_status moe_get_layout_noalloc(const moe_layout_cfg* cfg, const int32_t* topk
 /*  FP8_E4M3_POW2: as FP8_E4M3 but scale = 2^e, the smallest power of two   */
 /*    with a <= 448 * 2^e, and codes of the exactly scaled x * 2^-e (scales  */
 /*    that a GEMM can apply as exponent shifts).                            */
+/*  FP8_E4M3_UE8M0: the codes of FP8_E4M3_POW2, each scale 2^e stored as    */
+/*    one byte, e + 127 (the E8M0 encoding: the scale's biased fp32         */
+/*    exponent), a quarter of the scale bytes; the grouped-GEMM-friendly    */
+/*    form of the DeepEP V2 digest, "V2 release main changes" ("a new GEMM  */
+/*    layout").                                                             */
 /*  BF16: recv_x[p, :] = x[t, :] bit for bit.                               */
 /* Rows no pair addresses are not written.  pos of -1 (dropped) is skipped. */
 /*                                                                          */
 /* x           bf16 [T, H]                in                                */
 /* pos         int32 [T, k]               in (from moe_get_layout)          */
 /* recv_x      uint8 [N, H] (FP8) or bf16 [N, H]                 out        */
-/* recv_scales fp32 [N, H/128] (FP8 dtypes; NULL for BF16)        out        */
+/* recv_scales fp32 [N, H/128] (FP8_E4M3, FP8_E4M3_POW2; 4-byte aligned),   */
+/*             uint8 [N, H/128] (FP8_E4M3_UE8M0), NULL for BF16   out        */
 /* Limits: H % 128 == 0 (FP8 dtypes) or H % 8 == 0 (BF16); 1 <= k <= 64.    */
 /* ------------------------------------------------------------------------ */
 typedef struct {
@@ -227,7 +234,7 @@ typedef struct {
 } moe_dispatch_cfg;
 
 moe_status moe_dispatch(const moe_dispatch_cfg* cfg, const uint16_t* x, const int32_t* pos,
-                        void* recv_x, float* recv_scales, void* stream);
+                        void* recv_x, void* recv_scales, void* stream);
 
 /* ------------------------------------------------------------------------ */
 /* moe_combine -- top-k weighted gather-reduce back into token order.       */
@@ -331,7 +338,7 @@ moe_status moe_route_dispatch(const moe_route_cfg* route, const moe_layout_cfg* 
                               const moe_dispatch_cfg* dispatch, const float* logits,
                               const uint16_t* x, int32_t* topk_idx, float* topk_w, int32_t* cnt_e,
                               int32_t* cnt_r, int32_t* off_e, int32_t* off_r, int32_t* pos,
-                              int32_t* recv_src, int32_t* flags, void* recv_x, float* recv_scales,
+                              int32_t* recv_src, int32_t* flags, void* recv_x, void* recv_scales,
                               void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ */
@@ -469,10 +476,10 @@ moe_status moe_quantize_e4m3(const float* in, uint8_t* out, int64_t n, void* str
 
 const char* moe_status_string(moe_status status);
 const char* moe_last_error(void);
-/* moe_abi_version: 7 (adds moe_check_pow2_scales and the                  */
-/* MOE_FLAG_INCOMPLETE report of moe_route_dispatch to version 6, which     */
-/* added moe_get_layout_noalloc; version 5 added moe_layer_forward and      */
-/* moe_layer_workspace_bytes; no signature changed).                        */
+/* moe_abi_version: 8 (adds the MOE_DISPATCH_FP8_E4M3_UE8M0 dispatch dtype */
+/* to moe_dispatch and moe_route_dispatch, whose recv_scales became void*   */
+/* for it; version 7 added moe_check_pow2_scales and MOE_FLAG_INCOMPLETE,   */
+/* 6 moe_get_layout_noalloc, 5 moe_layer_forward and its workspace size).   */
 int32_t moe_abi_version(void);
 
 #ifdef __cplusplus

@@ -158,15 +158,17 @@ def layout(idx: np.ndarray, num_experts: int, num_ranks: int, capacity: int = 0,
     return out
 
 
-FP8, BF16, FP8_POW2 = 0, 1, 2
+FP8, BF16, FP8_POW2, FP8_UE8M0 = 0, 1, 2, 3
 
 
 def dispatch(x_bits: np.ndarray, pos: np.ndarray, num_recv_rows: int, dtype: int = FP8,
              recv_x: np.ndarray | None = None, recv_scales: np.ndarray | None = None):
     """x_bits: uint16 [T,H] bf16 patterns.  Returns (recv_x, recv_scales).
 
-    recv_x is uint8 [N,H] (FP8 codes) or uint16 [N,H] (BF16); rows that no pair
-    addresses keep the contents of the arrays passed in (zeros by default)."""
+    recv_x is uint8 [N,H] (FP8 codes) or uint16 [N,H] (BF16); recv_scales is
+    float32 [N,H/128], or uint8 [N,H/128] E8M0 bytes for FP8_UE8M0; rows that
+    no pair addresses keep the contents of the arrays passed in (zeros by
+    default)."""
     x_bits = np.ascontiguousarray(x_bits, dtype=np.uint16)
     pos = np.ascontiguousarray(pos, dtype=np.int32)
     T, H = x_bits.shape
@@ -174,8 +176,11 @@ def dispatch(x_bits: np.ndarray, pos: np.ndarray, num_recv_rows: int, dtype: int
     N = num_recv_rows
     if recv_x is None:
         recv_x = np.zeros((N, H), dtype=np.uint16 if dtype == BF16 else np.uint8)
+    sdt = np.uint8 if dtype == FP8_UE8M0 else np.float32
     if dtype != BF16 and recv_scales is None:
-        recv_scales = np.zeros((N, H // 128), dtype=np.float32)
+        recv_scales = np.zeros((N, H // 128), dtype=sdt)
+    if recv_scales is not None:
+        assert recv_scales.dtype == sdt and recv_scales.shape == (N, H // 128)
     sc = _p(recv_scales) if recv_scales is not None else None
     rc = lib().orc_dispatch(T, H, k, N, dtype, _p(x_bits), _p(pos), _p(recv_x), sc)
     if rc != 0:

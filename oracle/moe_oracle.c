@@ -367,7 +367,9 @@ int orc_layout(int T, int E, int k, int R, int C, int A, const int32_t* idx,
 /* Readings: OCP E4M3FN; one fp32 scale per 128 consecutive channels;        */
 /* a = max(amax, 2^-100); scale = a / 448 and inv = 448 / a (fp32, correctly */
 /* rounded); code = nearest E4M3FN of the fp32 product x * inv; the scales   */
-/* are a separate row-aligned [N, H/128] fp32 tensor.                        */
+/* are a separate row-aligned [N, H/128] fp32 tensor.  dtype 2 takes the      */
+/* power-of-two scale below instead, and dtype 3 stores that scale 2^e as    */
+/* the one byte e + 127 (E8M0), the grouped-GEMM-friendly form.             */
 /* ------------------------------------------------------------------------ */
 /* One block of 128 fp32 values -> E4M3FN codes with a power-of-two scale:
    a = max(max |v|, 2^-100); scale = 2^e, the smallest power of two with
@@ -386,7 +388,7 @@ static float quant_block_pow2(const float* v, uint8_t* q)
 }
 
 int orc_dispatch(int T, int H, int k, int N, int dtype, const uint16_t* x,
-                 const int32_t* pos, void* recv_x, float* recv_scales)
+                 const int32_t* pos, void* recv_x, void* recv_scales)
 {
     if (T < 0 || H <= 0 || k < 1 || N < 0) return -1;
     if (dtype == 1) {
@@ -401,7 +403,7 @@ int orc_dispatch(int T, int H, int k, int N, int dtype, const uint16_t* x,
             }
         return 0;
     }
-    if ((dtype != 0 && dtype != 2) || H % 128 != 0) return -1;
+    if ((dtype != 0 && dtype != 2 && dtype != 3) || H % 128 != 0) return -1;
     const int S = H / 128;
     uint8_t* out = (uint8_t*)recv_x;
     uint8_t q[128];
@@ -432,7 +434,10 @@ int orc_dispatch(int T, int H, int k, int N, int dtype, const uint16_t* x,
                 if (p < 0) continue;
                 if (p >= N) return -1;
                 memcpy(out + (size_t)p * H + (size_t)b * 128, q, 128);
-                recv_scales[(size_t)p * S + b] = scale;
+                if (dtype == 3)     /* E8M0: the power of two 2^e as the byte e + 127 */
+                    ((uint8_t*)recv_scales)[(size_t)p * S + b] = (uint8_t)(ilogbf(scale) + 127);
+                else
+                    ((float*)recv_scales)[(size_t)p * S + b] = scale;
             }
         }
     return 0;

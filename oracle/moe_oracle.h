@@ -73,9 +73,11 @@ int orc_layout(int T, int E, int k, int R, int C, int A, const int32_t* idx,
    recv_scales [N,H/128]); dtype 1: BF16 copy (recv_x as uint16 [N,H]);
    dtype 2: FP8 E4M3FN with power-of-two scales (the smallest 2^e with
    amax <= 448 * 2^e; codes of x / 2^e, exact scaling).
+   dtype 3: the codes of dtype 2, each scale 2^e stored as the byte e + 127
+   (E8M0), recv_scales uint8 [N, H/128].
    Rows whose pos is -1 are skipped; rows never addressed are left untouched. */
 int orc_dispatch(int T, int H, int k, int N, int dtype, const uint16_t* x,
-                 const int32_t* pos, void* recv_x, float* recv_scales);
+                 const int32_t* pos, void* recv_x, void* recv_scales);
 
 /* out[t,c] = bf16( sum_j w[t,j] * y[pos[t,j], c] ), sum in double; pos -1
    contributes nothing. */

@@ -37,7 +37,7 @@ def test_no_undefined_symbols_beyond_runtime():
 
 def test_status_strings_and_version():
     L = moe.lib()
-    assert L.moe_abi_version() == 7
+    assert L.moe_abi_version() == 8
     for s in (0, 1, 2, 4, 5):
         assert L.moe_status_string(s)
 
@@ -126,7 +126,7 @@ def test_check_pow2_scales_rejects():
 def test_dispatch_rejects():
     L = moe.lib()
     fake = ctypes.c_void_p(1 << 20)
-    for vals in [(4, 7168, 0, 32, 0, 0), (4, 100, 8, 32, 0, 0), (4, 7168, 8, 32, 3, 0),
+    for vals in [(4, 7168, 0, 32, 0, 0), (4, 100, 8, 32, 0, 0), (4, 7168, 8, 32, 4, 0),
                  (4, 12, 8, 32, 1, 0), (4, 7168, 8, 32, 0, 5), (-1, 7168, 8, 32, 0, 0)]:
         cfg = moe.DispatchCfg(*vals)
         assert L.moe_dispatch(ctypes.byref(cfg), fake, fake, fake, fake, None) == moe.MOE_ERR_INVALID

@@ -43,7 +43,7 @@ def sf(wl):
     return oracle.SOFTMAX if wl.score == "softmax" else oracle.SIGMOID
 
 
-ODT = {"fp8": oracle.FP8, "bf16": oracle.BF16, "fp8_pow2": oracle.FP8_POW2}
+ODT = {"fp8": oracle.FP8, "bf16": oracle.BF16, "fp8_pow2": oracle.FP8_POW2, "fp8_ue8m0": oracle.FP8_UE8M0}
 
 
 def reference(wl, logits, x, align=0, dtype=None):
@@ -54,7 +54,10 @@ def reference(wl, logits, x, align=0, dtype=None):
     N = moe.recv_rows(wl.T, wl.E, wl.k, wl.capacity, align)
     fp8 = dtype != "bf16"
     rx = np.full((N, wl.H), FILL8 if fp8 else np.uint16(FILL16 & 0xFFFF), np.uint8 if fp8 else np.uint16)
-    rs = np.full((N, wl.S), FILLS, np.float32) if fp8 else None
+    if dtype == "fp8_ue8m0":
+        rs = np.full((N, wl.S), 0xEE, np.uint8)
+    else:
+        rs = np.full((N, wl.S), FILLS, np.float32) if fp8 else None
     rx, rs = oracle.dispatch(x, lay["pos"], N, ODT[dtype], rx, rs)
     return idx, w, lay, rx, rs, N
 
@@ -69,7 +72,10 @@ def prefilled_out(wl, N, dtype, align=0):
     rx = torch.full((N, wl.H), FILL8 if fp8 else FILL16, dtype=torch.uint8 if fp8 else torch.int16, device=DEV)
     if not fp8:
         rx = rx.view(torch.bfloat16)
-    rs = torch.full((N, wl.S), FILLS, dtype=torch.float32, device=DEV) if fp8 else None
+    if dtype == "fp8_ue8m0":
+        rs = torch.full((N, wl.S), 0xEE, dtype=torch.uint8, device=DEV)
+    else:
+        rs = torch.full((N, wl.S), FILLS, dtype=torch.float32, device=DEV) if fp8 else None
     return idx, w, lay, rx, rs
 
 
@@ -85,7 +91,7 @@ def check(wl, got, ref, dtype):
         assert np.array_equal(bf16_from_dev(rx), rrx), "recv_x"
     else:
         assert np.array_equal(rx.cpu().numpy(), rrx), "recv_x"
-        assert np.array_equal(rs.cpu().numpy().view(np.uint32), rrs.view(np.uint32)), "recv_scales"
+        assert np.array_equal(rs.cpu().numpy().view(np.uint8), rrs.view(np.uint8)), "recv_scales"
 
 
 def run_case(wl, align=0, dtype=None, logits=None, x=None, ws=None):
@@ -126,7 +132,7 @@ def test_route_dispatch_parity(wl):
     run_case(wl)
 
 
-@pytest.mark.parametrize("dtype", ["fp8_pow2", "bf16"])
+@pytest.mark.parametrize("dtype", ["fp8_pow2", "fp8_ue8m0", "bf16"])
 def test_route_dispatch_dtypes(dtype):
     wl = W.get("ll_decode")
     say(f"[gpu] route_dispatch ll_decode {dtype}")

@@ -52,6 +52,8 @@ MUTANTS = {
         "const double r = nearbyint(a / q) * q;", "const double r = floor(a / q) * q;"),
     "pow2 scale: chosen against 256 instead of 448": (
         "while (ldexp(448.0, e) < (double)a) ++e;", "while (ldexp(256.0, e) < (double)a) ++e;"),
+    "ue8m0: exponent bias 126": (
+        "(uint8_t)(ilogbf(scale) + 127);", "(uint8_t)(ilogbf(scale) + 126);"),
     "combine: weights of reversed slots": (
         "acc += (double)w[(size_t)t * k + j] *", "acc += (double)w[(size_t)t * k + (k - 1 - j)] *"),
     "dispatch backward: last slot overwrites": (

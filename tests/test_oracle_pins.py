@@ -749,3 +749,26 @@ def test_dispatch_pow2_scales(orc):
     vals = np.array([orc.e4m3_value(c) for c in range(256)])
     deq = vals[q].reshape(wl.T, wl.S, 128) * sc.astype(np.float64)[:, :, None]
     assert np.all(np.abs(xf - deq) <= 2 ** -4 * np.abs(xf) + 2 ** -10 * sc[:, :, None])
+
+
+def test_dispatch_ue8m0_bytes(orc):
+    """E8M0 mode: the codes of the power-of-two mode, and each scale 2^e as the
+    byte e + 127.  Hand-derived blocks: amax 1 -> the smallest 2^e with
+    1 <= 448 * 2^e is 2^-8 (448/256 = 1.75 >= 1 > 0.875), byte 119; amax 448
+    -> 2^0, byte 127; amax 450 -> 2^1, byte 128; a zero block (amax floored
+    at 2^-100) -> 2^-108 (448 * 2^-108 = 1.75 * 2^-100), byte 19."""
+    wl = _dsv3_small(T=64, H=1024)
+    x = W.gen_x(wl)
+    x[3, :128] = 0
+    x[4, 384:512] = W.f32_to_bf16_bits(np.full(128, 1.0, np.float32))
+    x[5, 128:256] = W.f32_to_bf16_bits(np.full(128, 448.0, np.float32))
+    x[6, 256:384] = W.f32_to_bf16_bits(np.full(128, 450.0, np.float32))
+    pos = np.arange(wl.T, dtype=np.int32)[:, None]
+    q2, sc2 = orc.dispatch(x, pos, wl.T, dtype=orc.FP8_POW2)
+    q3, sc3 = orc.dispatch(x, pos, wl.T, dtype=orc.FP8_UE8M0)
+    assert sc3.dtype == np.uint8 and sc3.shape == sc2.shape
+    assert np.array_equal(q2, q3)
+    assert np.array_equal(np.ldexp(1.0, sc3.astype(np.int64) - 127), sc2.astype(np.float64))
+    assert sc3[4, 3] == 119 and sc3[5, 1] == 127 and sc3[6, 2] == 128 and sc3[3, 0] == 19
+    # the scale stream is a quarter of the fp32 one
+    assert sc3.nbytes * 4 == sc2.nbytes
