@@ -20,10 +20,9 @@ namespace {
 
 constexpr int kUnit = 512;
 
-// cache policy of the grad_y writes (1 = streaming)
-#ifndef CGL_BWD_STORE_NT
-#define CGL_BWD_STORE_NT 1
-#endif
+// cache policy of the grad_y writes: streaming (measured: 4 us faster here and
+// 10 us in the following kernel, whose reads the plain stores would evict)
+constexpr int kBwdStoreNT = 1;
 
 struct CombineBwdArgs {
     const uint16_t* grad_out;
@@ -99,7 +98,7 @@ __device__ __forceinline__ void bwd_chunk(const u32x4 (&gv)[U], const uint16_t* 
             o.y = pack2(wj, gv[u].y);
             o.z = pack2(wj, gv[u].z);
             o.w = pack2(wj, gv[u].w);
-            store_stream<CGL_BWD_STORE_NT>(o, (u32x4*)(dyrow + c));
+            store_stream<kBwdStoreNT>(o, (u32x4*)(dyrow + c));
             dot = __builtin_fmaf(bf16_lo(gv[u].x), bf16_lo(yv[u].x), dot);
             dot = __builtin_fmaf(bf16_hi(gv[u].x), bf16_hi(yv[u].x), dot);
             dot = __builtin_fmaf(bf16_lo(gv[u].y), bf16_lo(yv[u].y), dot);

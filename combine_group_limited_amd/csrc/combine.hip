@@ -18,10 +18,14 @@
 namespace cgl {
 namespace {
 
-template <int U, int KC>
+template <int U, int KC, bool ALL = false>
 __global__ __launch_bounds__(kCombineThreads) void combine_kernel(CombineArgs a) {
-    combine_wave<U, KC>(a, blockIdx.x * (kCombineThreads / kWave) + wave_in_block());
+    combine_wave<U, KC, ALL>(a, blockIdx.x * (kCombineThreads / kWave) + wave_in_block());
 }
+
+// Grids below this many waves issue all k slots' gathers at once (k = 8, 4 or
+// 2, one unit per wave): decode-sized batches.
+constexpr long long kAllSlotsWaves = 2048;
 
 template <int U>
 hipError_t launch_u(CombineArgs a, hipStream_t s) {
@@ -29,11 +33,22 @@ hipError_t launch_u(CombineArgs a, hipStream_t s) {
     const long long waves = (long long)a.T * a.chunks;
     const int wpb = kCombineThreads / kWave;
     const unsigned blocks = (unsigned)((waves + wpb - 1) / wpb);
+    if constexpr (U == 1) {
+        if (waves < kAllSlotsWaves) switch (a.k) {
+            case 8: hipLaunchKernelGGL((combine_kernel<U, 8, true>), dim3(blocks), dim3(kCombineThreads), 0, s, a);
+                return hipGetLastError();
+            case 4: hipLaunchKernelGGL((combine_kernel<U, 4, true>), dim3(blocks), dim3(kCombineThreads), 0, s, a);
+                return hipGetLastError();
+            case 2: hipLaunchKernelGGL((combine_kernel<U, 2, true>), dim3(blocks), dim3(kCombineThreads), 0, s, a);
+                return hipGetLastError();
+            default: break;
+        }
+    }
     switch (a.k) {
-        case 8: hipLaunchKernelGGL((combine_kernel<U, 8>), dim3(blocks), dim3(kCombineThreads), CGL_COMBINE_LDS_CAP, s, a); break;
-        case 4: hipLaunchKernelGGL((combine_kernel<U, 4>), dim3(blocks), dim3(kCombineThreads), CGL_COMBINE_LDS_CAP, s, a); break;
-        case 2: hipLaunchKernelGGL((combine_kernel<U, 2>), dim3(blocks), dim3(kCombineThreads), CGL_COMBINE_LDS_CAP, s, a); break;
-        default: hipLaunchKernelGGL((combine_kernel<U, 0>), dim3(blocks), dim3(kCombineThreads), CGL_COMBINE_LDS_CAP, s, a); break;
+        case 8: hipLaunchKernelGGL((combine_kernel<U, 8>), dim3(blocks), dim3(kCombineThreads), 0, s, a); break;
+        case 4: hipLaunchKernelGGL((combine_kernel<U, 4>), dim3(blocks), dim3(kCombineThreads), 0, s, a); break;
+        case 2: hipLaunchKernelGGL((combine_kernel<U, 2>), dim3(blocks), dim3(kCombineThreads), 0, s, a); break;
+        default: hipLaunchKernelGGL((combine_kernel<U, 0>), dim3(blocks), dim3(kCombineThreads), 0, s, a); break;
     }
     return hipGetLastError();
 }
