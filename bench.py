@@ -248,7 +248,8 @@ def backward_main(args, wl, moe, torch, dev, sets, hev, stream):
         "metric": "combine_backward+dispatch_backward effective HBM GB/s, " + wl.name,
         "value": round(tot / ((cb_us + db_us) * 1e-6) / 1e9, 1), "unit": "GB/s", "n_gpus": 1,
         "steps": K, "warmup": args.warmup, "ms_per_step": round(hev.ms(start, end) / K, 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp32",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16 gradients (fp32 arithmetic)",
         "data": "synthetic (seeded N(0,1) bf16 gradients and expert outputs)",
         "config": {"workload": W.describe(wl), "direction": "backward"},
         "combine_backward_us": round(cb_us, 2), "dispatch_backward_us": round(db_us, 2),
@@ -535,6 +536,27 @@ def main():
     torch.cuda.synchronize()
     ms_step_plain = hev.ms(start2, end2) / K
 
+    # dispatch -> combine back to back: one event pair around the two kernels,
+    # none between them (route and layout run first, outside the pair)
+    evs_b2b = [hev.create(2) for _ in range(K)]
+
+    def step_b2b(i, ev):
+        x, logits, y = sets[i % 2]
+        moe.route_topk(logits, wl.G, wl.g, wl.k, wl.score, out=(idx, wts))
+        lay = moe.get_layout(idx, wl.E, wl.R, wl.capacity, out=lay_out)
+        hev.record(ev[0], stream)
+        moe.dispatch(x, lay.pos, N, wl.dtype, recv_x, recv_s)
+        moe.combine(y, lay.pos, wts, out)
+        hev.record(ev[1], stream)
+
+    torch.cuda.synchronize()
+    if hasattr(torch.cuda, "_sleep"):
+        torch.cuda._sleep(int(2e7))
+    for i in range(K):
+        step_b2b(i, evs_b2b[i])
+    torch.cuda.synchronize()
+    b2b_us = np.array([hev.ms(e[0], e[1]) for e in evs_b2b]) * 1e3
+
     # cold-cache pass: before every step, outside its stage events, a 1 GiB
     # scratch read evicts everything from the L2s and the 256 MB last-level
     # cache (a read, not a write, so no dirty flush lines are left behind for
@@ -547,8 +569,33 @@ def main():
         torch.sum(flush, dim=0, out=flush_sum)
         step(i, evs_cold[i])
     torch.cuda.synchronize()
-    del flush
     cold = np.array([[hev.ms(e[q], e[q + 1]) for q in range(4)] for e in evs_cold]) * 1e3  # us
+
+    # write-back included: dispatch -> combine followed, inside the same event
+    # pair, by the 1 GiB read, which evicts the dirty receive rows and output
+    # from the last-level cache (so their write-back to HBM lands inside the
+    # pair); minus the same read timed after a clean read
+    evs_wb = [hev.create(2) for _ in range(K)]
+    evs_rd = [hev.create(2) for _ in range(K)]
+    torch.cuda.synchronize()
+    for i in range(K):
+        x, logits, y = sets[i % 2]
+        torch.sum(flush, dim=0, out=flush_sum)
+        moe.route_topk(logits, wl.G, wl.g, wl.k, wl.score, out=(idx, wts))
+        lay = moe.get_layout(idx, wl.E, wl.R, wl.capacity, out=lay_out)
+        hev.record(evs_wb[i][0], stream)
+        moe.dispatch(x, lay.pos, N, wl.dtype, recv_x, recv_s)
+        moe.combine(y, lay.pos, wts, out)
+        torch.sum(flush, dim=0, out=flush_sum)
+        hev.record(evs_wb[i][1], stream)
+        torch.sum(flush, dim=0, out=flush_sum)
+        hev.record(evs_rd[i][0], stream)
+        torch.sum(flush, dim=0, out=flush_sum)
+        hev.record(evs_rd[i][1], stream)
+    torch.cuda.synchronize()
+    del flush
+    wb_us = np.array([hev.ms(e[0], e[1]) for e in evs_wb]) * 1e3
+    rd_us = np.array([hev.ms(e[0], e[1]) for e in evs_rd]) * 1e3
 
     ms_step = hev.ms(start, end) / K
     stage = np.array([[hev.ms(e[q], e[q + 1]) for q in range(4)] for e in evs])  # ms
@@ -582,7 +629,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp32",
+        "dtype": ("fp8-e4m3 dispatch" if fp8 else "bf16 dispatch") + ", bf16 combine (fp32 arithmetic)",
         "data": "synthetic (seeded N(0,1) bf16 tokens and expert outputs, N(0,1) fp32 router logits)",
         "config": {"workload": W.describe(wl), "tokens": wl.T, "hidden": wl.H, "experts": wl.E,
                    "groups": wl.G, "topk_group": wl.g, "topk": wl.k, "virtual_ranks": wl.R,
@@ -603,6 +650,21 @@ def main():
         "median_dispatch_plus_combine_us": round(float(np.median(stage[:, 2] + stage[:, 3])) * 1e3, 2),
         "wall_s_timed_region": round(t_wall, 4),
         "roofline": roof,
+        "back_to_back": {
+            "dispatch_plus_combine_us": round(float(b2b_us.mean()), 2),
+            "median_us": round(float(np.median(b2b_us)), 2),
+            "gbps": round(dc_bytes / (float(b2b_us.mean()) * 1e-6) / 1e9, 1),
+            "note": "one event pair around dispatch and combine, no event between them",
+        },
+        "with_write_back": {
+            "dispatch_plus_combine_us": round(float((wb_us - rd_us).mean()), 2),
+            "gbps": round(dc_bytes / (float((wb_us - rd_us).mean()) * 1e-6) / 1e9, 1),
+            "pair_plus_read_us": round(float(wb_us.mean()), 2),
+            "clean_read_us": round(float(rd_us.mean()), 2),
+            "note": "dispatch, combine and a 1 GiB read inside one event pair (the read evicts the dirty "
+                    "receive rows and outputs, so their write-back is inside), minus the same read after "
+                    "a clean read",
+        },
         "cold_cache": {
             "dispatch_us": round(float(cold[:, 2].mean()), 2),
             "combine_us": round(float(cold[:, 3].mean()), 2),
