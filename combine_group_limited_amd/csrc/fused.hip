@@ -11,13 +11,12 @@
 //
 // One launch of 256-thread blocks, all resident at once (the host sizes the
 // grid from the occupancy of this kernel, with a factor-two margin):
-//   1. every wave loads its first 512-channel unit of x (inputs only), and the
-//      waves 0..T-1 route token = wave index (route_impl.hpp); the unit is
-//      quantised while the routing loads are in flight;
+//   1. waves 0..T-1 route token = wave index (route_impl.hpp);
 //   2. a grid-wide barrier (below);
-//   3. every block rebuilds the whole layout of the batch in LDS (T <= 1024:
-//      a 64-bit token mask per expert and 64-token chunk, popcount ranks, a
-//      block-wide scan), which is cheaper than a second barrier;
+//   3. every wave loads its first 512-channel unit of x, and while those loads
+//      are in flight every block rebuilds the whole layout of the batch in LDS
+//      (T <= 1024: a 64-bit token mask per expert and 64-token chunk, popcount
+//      ranks, a block-wide scan), which is cheaper than a second barrier;
 //   4. every wave stores its unit(s) into the token's k receive rows;
 //   5. the layout outputs are split between blocks so that every element is
 //      written by exactly one block (block 0: counts, offsets and flags;
@@ -117,12 +116,8 @@ __global__ __launch_bounds__(kFusedThreads) void fused_decode_kernel(FusedArgs a
     // a workspace an earlier launch gave up on is refused at the barrier
     const bool refused = tid == 0 && barrier_gave_up(a.bar);
 
-    // ---- 1. first unit of x (independent of the routing), then routing ----
-    u32x4 v0 = u32x4{0u, 0u, 0u, 0u};
-    if (gw < items) v0 = load_unit(a, gw, lane);
+    // ---- 1. routing ------------------------------------------------------------
     for (int t = gw; t < T; t += nw) route_token<EPL, LPG, true>(a.r, t);
-    float s0 = 0.0f;
-    const u32x2 q0 = quantize(a, v0, s0);
 
     // ---- 2. every token routed ---------------------------------------------
     if (!grid_barrier<false>(a.bar, refused)) {  // block-uniform
@@ -133,18 +128,32 @@ __global__ __launch_bounds__(kFusedThreads) void fused_decode_kernel(FusedArgs a
     // a block of this launch that stopped waiting as the barrier opened
     const bool gave_up = blockIdx.x == 0 && tid == 0 && barrier_gave_up(a.bar);
 
+    // first unit of x, in flight while the layout is built
+    u32x4 v0 = u32x4{0u, 0u, 0u, 0u};
+    if (gw < items) v0 = load_unit(a, gw, lane);
+
     // ---- 3. the layout of the whole batch, in LDS ----------------------------
     for (int i = tid; i < a.nch * E; i += kFusedThreads) emask[i] = 0;
     for (int i = tid; i < a.nch * R; i += kFusedThreads) rmask[i] = 0;
     __syncthreads();
     const int Er = E / R;
     int bad = 0;
-    for (int t = tid; t < T; t += kFusedThreads) {
-        const uint64_t bit = 1ull << (t & 63);
-        const int ch = t >> 6;
-        for (int j = 0; j < k; ++j) {
-            const int e = __hip_atomic_load(&a.r.idx[(size_t)t * k + j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            posl[t * k + j] = e;
+    // four consecutive pairs per thread, their device-scope loads all issued
+    // before the first is used (one load in flight per slot costs 1.3 us)
+    for (int i0 = 4 * tid; i0 < T * k; i0 += 4 * kFusedThreads) {
+        int ev[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+            ev[c] = i0 + c < T * k ? __hip_atomic_load(&a.r.idx[i0 + c], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                                   : 0;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const int i = i0 + c;
+            if (i >= T * k) break;
+            const int t = i / k, e = ev[c];
+            const uint64_t bit = 1ull << (t & 63);
+            const int ch = t >> 6;
+            posl[i] = e;
             if (e < 0 || e >= E) {
                 bad = 1;
                 continue;
@@ -179,6 +188,8 @@ __global__ __launch_bounds__(kFusedThreads) void fused_decode_kernel(FusedArgs a
     __syncthreads();
 
     // ---- 4. dispatch ----------------------------------------------------------
+    float s0 = 0.0f;
+    const u32x2 q0 = quantize(a, v0, s0);
     if (gw < items) store_unit(a, posl, gw, lane, v0, q0, s0);
     for (int item = gw + nw; item < items; item += nw) {
         const u32x4 v = load_unit(a, item, lane);

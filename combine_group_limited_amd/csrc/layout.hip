@@ -324,8 +324,9 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_position_kernel(LayoutA
 // grid-wide fill precedes the positions.
 // Per pair the expert blocks spend three compares (below e, equal to e, on
 // rank e), unsigned so that out-of-range indices count nowhere.
+// Blocks of NT threads: 1024 in general, 128 or 256 for batches that fit one
+// iteration (fewer waves to launch and to meet at each barrier).
 constexpr int kExpertLayoutThreads = 1024;
-constexpr int kExpertLayoutWaves = kExpertLayoutThreads / kWave;
 constexpr int kExpertLayoutMaxIters = 32;
 constexpr int kExpertLayoutMaxTokens = kExpertLayoutThreads * kExpertLayoutMaxIters;
 constexpr int kExpertLayoutBatch = 4;  // iterations whose loads are in flight together
@@ -343,24 +344,25 @@ __device__ __forceinline__ int wave_scan_dpp(int v) {
     return v + (row >= 1 ? r0 : 0) + (row >= 2 ? r1 : 0) + (row >= 3 ? r2 : 0);
 }
 
-template <int KT>
-__global__ __launch_bounds__(kExpertLayoutThreads) void layout_expert_kernel(LayoutArgs a) {
-    __shared__ uint64_t ballots[kExpertLayoutMaxIters * kExpertLayoutWaves];
-    __shared__ int32_t base[kExpertLayoutMaxIters * kExpertLayoutWaves];
-    __shared__ int8_t slot[kExpertLayoutMaxIters * kExpertLayoutThreads];  // slot of e in the token, or -1
-    __shared__ int32_t hist[512];                                             // expert 0, padded: counts
-    __shared__ int32_t red[2][kExpertLayoutWaves];
+template <int KT, int NT>
+__global__ __launch_bounds__(NT) void layout_expert_kernel(LayoutArgs a) {
+    constexpr int kWaves = NT / kWave, kMaxIters = kExpertLayoutMaxTokens / NT;
+    __shared__ uint64_t ballots[kMaxIters * kWaves];
+    __shared__ int32_t base[kMaxIters * kWaves];
+    __shared__ int8_t slot[kExpertLayoutMaxTokens];  // slot of e in the token, or -1
+    __shared__ int32_t hist[512];                    // expert 0, padded: counts
+    __shared__ int32_t red[2][kWaves];
     __shared__ int32_t total;
     const int e = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int T = a.T, k = KT > 0 ? KT : a.k;
-    const int iters = (T + kExpertLayoutThreads - 1) / kExpertLayoutThreads;
+    const int iters = (T + NT - 1) / NT;
     const int Er = a.E / a.R;
     const bool rank_block = e < a.R;
     const unsigned r0 = (unsigned)(e * Er);  // first expert of rank e (rank blocks)
     const bool check = e == 0;               // block-uniform
     const bool count_all = check && a.C > 0;
     if (count_all) {
-        for (int i = tid; i < a.E; i += kExpertLayoutThreads) hist[i] = 0;
+        for (int i = tid; i < a.E; i += NT) hist[i] = 0;
         __syncthreads();
     }
 
@@ -369,14 +371,14 @@ __global__ __launch_bounds__(kExpertLayoutThreads) void layout_expert_kernel(Lay
         TokenRow<KT> rows[kExpertLayoutBatch];
 #pragma unroll
         for (int b = 0; b < kExpertLayoutBatch; ++b) {
-            const int t = (it0 + b) * kExpertLayoutThreads + tid;
+            const int t = (it0 + b) * NT + tid;
             if (KT > 0 && it0 + b < iters && t < T) rows[b].load(a.idx + (size_t)t * k);
         }
 #pragma unroll
         for (int b = 0; b < kExpertLayoutBatch; ++b) {
             const int it = it0 + b;
             if (it >= iters) break;  // block-uniform
-            const int t = it * kExpertLayoutThreads + tid;
+            const int t = it * NT + tid;
             int js = -1;
             if (t < T) {
                 bool hit_rank = false;
@@ -412,16 +414,16 @@ __global__ __launch_bounds__(kExpertLayoutThreads) void layout_expert_kernel(Lay
                             if (!bad_pair(j)) atomicAdd(&hist[KT > 0 ? rows[b].e[j] : a.idx[(size_t)t * k + j]], 1);
                 }
             }
-            slot[it * kExpertLayoutThreads + tid] = (int8_t)js;
+            slot[it * NT + tid] = (int8_t)js;
             const uint64_t bal = __ballot(js >= 0);
-            if (lane == 0) ballots[it * kExpertLayoutWaves + w] = bal;
+            if (lane == 0) ballots[it * kWaves + w] = bal;
         }
     }
     if (check) {
         int over = 0;
         if (count_all) {
             __syncthreads();  // every pair counted
-            for (int i = tid; i < a.E; i += kExpertLayoutThreads) over |= hist[i] > a.C;
+            for (int i = tid; i < a.E; i += NT) over |= hist[i] > a.C;
         }
         const int any_over = __syncthreads_or(over);
         const int any_bad = __syncthreads_or(bad);
@@ -435,7 +437,7 @@ __global__ __launch_bounds__(kExpertLayoutThreads) void layout_expert_kernel(Lay
     }
     __syncthreads();
     // exclusive scan of the ballots' popcounts over (iteration, wave), by wave 0
-    const int nb = iters * kExpertLayoutWaves;
+    const int nb = iters * kWaves;
     if (w == 0) {
         int carry = 0;
         for (int i0 = 0; i0 < nb; i0 += kWave) {
@@ -450,7 +452,7 @@ __global__ __launch_bounds__(kExpertLayoutThreads) void layout_expert_kernel(Lay
     __syncthreads();
     int off = 0, cr = 0;
 #pragma unroll
-    for (int q = 0; q < kExpertLayoutWaves; ++q) {
+    for (int q = 0; q < kWaves; ++q) {
         off += red[0][q];
         cr += red[1][q];
     }
@@ -459,10 +461,10 @@ __global__ __launch_bounds__(kExpertLayoutThreads) void layout_expert_kernel(Lay
     // positions and receive rows of expert e's pairs
     const uint64_t below = (1ull << lane) - 1ull;
     for (int it = 0; it < iters; ++it) {
-        const int js = slot[it * kExpertLayoutThreads + tid];
+        const int js = slot[it * NT + tid];
         if (js < 0) continue;
-        const int t = it * kExpertLayoutThreads + tid;
-        const int i = it * kExpertLayoutWaves + w;
+        const int t = it * NT + tid;
+        const int i = it * kWaves + w;
         const int rank = base[i] + __popcll(ballots[i] & below);
         int p;
         if (a.C == 0)
@@ -474,7 +476,7 @@ __global__ __launch_bounds__(kExpertLayoutThreads) void layout_expert_kernel(Lay
     }
     // padded: this expert's empty rows
     if (a.C > 0)
-        for (int r = min(cnt, a.C) + tid; r < a.C; r += kExpertLayoutThreads) a.recv_src[(size_t)e * a.C + r] = -1;
+        for (int r = min(cnt, a.C) + tid; r < a.C; r += NT) a.recv_src[(size_t)e * a.C + r] = -1;
 
     // counts and offsets
     if (tid == 0) {
@@ -492,10 +494,25 @@ size_t lds_bytes(int E, int R, bool with_table) {
            sizeof(int32_t) * (3 * (size_t)E + 1);
 }
 
+// The per-expert kernel's time grows with the batch (every block walks all of
+// it) and hardly with E; the two-pass kernels split the batch over blocks.
+// Measured back to back: 4096 tokens top-8, E 8..256: 9.2-9.6 us against
+// 11.1-12.6 us; 16384 tokens top-2: E <= 64 10.9-11.4 us against 9.7-10.3 us,
+// E 128 and 256 10.7-10.9 us against 17.4-18.0 us.
+inline bool use_expert_layout(const LayoutArgs& a) {
+    return a.A <= 1 && a.T > 0 && a.T <= kExpertLayoutMaxTokens && (a.T <= 8192 || a.E > 64);
+}
+
 template <int KT>
 hipError_t launch_kt(LayoutArgs a, hipStream_t stream) {
-    if (a.A <= 1 && a.T > 0 && a.T <= kExpertLayoutMaxTokens) {
-        hipLaunchKernelGGL((layout_expert_kernel<KT>), dim3(a.E), dim3(kExpertLayoutThreads), 0, stream, a);
+    if (use_expert_layout(a)) {
+        if (a.T <= 128)
+            hipLaunchKernelGGL((layout_expert_kernel<KT, 128>), dim3(a.E), dim3(128), 0, stream, a);
+        else if (a.T <= 256)
+            hipLaunchKernelGGL((layout_expert_kernel<KT, 256>), dim3(a.E), dim3(256), 0, stream, a);
+        else
+            hipLaunchKernelGGL((layout_expert_kernel<KT, kExpertLayoutThreads>), dim3(a.E),
+                               dim3(kExpertLayoutThreads), 0, stream, a);
         return hipGetLastError();
     }
     if (a.NB <= 1) {
