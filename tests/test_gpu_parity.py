@@ -333,11 +333,19 @@ def random_idx(T, E, k, seed):
 
 
 @pytest.mark.parametrize("T,E,k,R,C", [
-    (1, 256, 8, 32, 0), (1023, 256, 8, 32, 0), (1025, 64, 4, 8, 0), (32768, 16, 2, 4, 0),
-    (32769, 16, 2, 4, 0),          # above the one-launch limit: the two-launch path
+    (1, 256, 8, 32, 0),
+    (127, 256, 8, 32, 128), (128, 256, 8, 32, 0),    # 128-thread blocks
+    (129, 256, 8, 32, 128), (256, 256, 8, 32, 0),    # 256-thread blocks
+    (257, 64, 4, 8, 64), (1023, 256, 8, 32, 0), (1025, 64, 4, 8, 0),
+    (8192, 16, 2, 4, 0),           # the largest one-launch batch over few experts
+    (8193, 64, 2, 8, 0),           # two-pass: above 8192 tokens over at most 64 experts
+    (8193, 80, 2, 8, 0),           # one launch again above 64 experts
+    (32768, 16, 2, 4, 0),          # two-pass
+    (32769, 16, 2, 4, 0),          # above the one-launch limit: two-pass
     (32768, 512, 3, 8, 0),         # general k, the most tokens and experts of the one launch
     (5000, 256, 8, 32, 20),        # padded, overflowing experts
-    (32768, 64, 1, 64, 600),       # padded at the one-launch limit, k = 1
+    (32768, 64, 1, 64, 600),       # padded, two-pass, k = 1
+    (32768, 128, 1, 64, 300),      # padded at the one-launch limit, k = 1
 ])
 def test_layout_token_limits(T, E, k, R, C):
     say(f"[gpu] layout T={T} E={E} k={k} R={R} C={C}")
