@@ -327,6 +327,38 @@ def test_layout_flags_bad_indices():
     assert int(lay.flags.item()) == moe.FLAG_BAD_INDEX
 
 
+@pytest.mark.parametrize("T,E,k,C,kind", [
+    (100, 256, 8, 128, "dup"), (100, 256, 8, 128, "range"),  # 128-thread blocks, padded
+    (200, 64, 4, 0, "dup"), (200, 64, 4, 0, "range"),        # 256-thread blocks
+    (5000, 256, 8, 0, "dup"), (5000, 256, 8, 0, "range"),    # 1024-thread blocks, several iterations
+    (5000, 256, 8, 40, "range"),                              # padded, overflowing and bad
+    (20000, 16, 2, 0, "dup"),                                 # two-pass kernels
+])
+def test_layout_flags_bad_indices_every_kernel(T, E, k, C, kind):
+    """One repeated or out-of-range index late in the batch raises the flag in
+    every layout kernel; every pos the call writes stays in [-1, N)."""
+    say(f"[gpu] layout bad index {kind} T={T} E={E} k={k} C={C}")
+    idx = random_idx(T, E, k, T + k)
+    t = T - 3
+    if kind == "dup":
+        idx[t, k - 1] = idx[t, 0]
+    else:
+        idx[t, k // 2] = E + 5
+    lay = moe.get_layout(torch.from_numpy(idx).to(DEV), E, 4, C)
+    flags = int(lay.flags.item())
+    assert flags & moe.FLAG_BAD_INDEX
+    N = E * C if C > 0 else T * k
+    pos = lay.pos.cpu().numpy()
+    assert pos.min() >= -1 and pos.max() < N
+    # the clean pairs of the other tokens are placed exactly as the oracle places them
+    ok = np.ones(T, bool)
+    ok[t] = False
+    ref = oracle.layout(np.delete(idx, t, axis=0), E, 4, C)
+    if C == 0:
+        return  # compact offsets count the bad token's pairs too; only padded rows are token-local
+    assert np.array_equal(pos[ok][:t], ref["pos"][:t])
+
+
 def random_idx(T, E, k, seed):
     """k distinct experts per token: the first k of a seeded random order."""
     return np.argsort(np.random.default_rng(seed).random((T, E)), axis=1)[:, :k].astype(np.int32)
