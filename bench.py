@@ -740,6 +740,16 @@ def main():
                 torch.cuda.synchronize()
                 res["one_launch_decode"][name] = round(hev.ms(gs, ge) / K * 1e3, 2)
                 del graph
+            # host-driven loop: K steps submitted one after another from Python
+            # with the GPU not held, wall clock to the final synchronise; the
+            # per-call host cost of the binding then sets the pace
+            for name, fn in (("host_loop_step_us_separate", step), ("host_loop_step_us_one_launch", fstep)):
+                torch.cuda.synchronize()
+                t0 = time.perf_counter()
+                for i in range(K):
+                    fn(i)
+                torch.cuda.synchronize()
+                res["one_launch_decode"][name] = round((time.perf_counter() - t0) / K * 1e6, 2)
         except moe.MoeError as e:
             res["one_launch_decode"] = {"unsupported": str(e)}
 
