@@ -13,11 +13,11 @@ enqueued, so the timeline holds only GPU work.  A third pass of K steps, each
 preceded by a 1 GiB scratch read, reports the same stages with cold caches.
 For batches of at most 1024 tokens a fourth pass times the step with route,
 layout and dispatch in one launch (moe_route_dispatch), and both decode steps
-are also timed captured in a HIP graph and submitted one by one from the host
-with the GPU not held (where the per-call host cost sets the pace).  HIP events on the launch
-stream (created without the system-scope fence) bracket every stage of every
-timed step; a second pass of K steps without them gives the step time free of
-their cost.
+are also timed captured in a HIP graph and submitted one by one from the
+host with the GPU not held (where the per-call host cost sets the pace).  HIP
+events on the launch stream (created without the system-scope fence) bracket
+every stage of every timed step; a second pass of K steps without them gives
+the step time free of their cost.
 
 Prints one JSON line.  ``value`` is the effective HBM bandwidth of dispatch +
 combine: their algorithmic bytes over their measured time.
