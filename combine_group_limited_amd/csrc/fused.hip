@@ -30,6 +30,9 @@
 // block arrives.  Device-scope release/acquire fences would instead write back
 // and invalidate each XCD's whole L2 once per block: measured on MI355X at
 // 128 tokens, they cost 11 us of a 17 us launch.
+#include <mutex>
+#include <vector>
+
 #include "dispatch_impl.hpp"
 #include "grid_barrier.hpp"
 #include "moe_internal.hpp"
@@ -238,6 +241,41 @@ size_t fused_lds_bytes(int T, int E, int k, int R) {
     return 8 * nch * (E + R) + 4 * ((size_t)E + E + 1 + (size_t)T * k + kSliceRows);
 }
 
+// Blocks of a kernel that the current device holds at once with the given
+// dynamic LDS: asked of the runtime once per (device, kernel, LDS size) and
+// then kept, since a decode loop calls this path every step and the query
+// costs host time of the order of the kernel itself.
+template <class K>
+hipError_t resident_blocks(K kern, size_t lds, long long* out) {
+    struct Entry {
+        int dev;
+        const void* kern;
+        size_t lds;
+        long long blocks;
+    };
+    static std::mutex mu;
+    static std::vector<Entry> cache;
+    int dev = 0;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess) return err;
+    {
+        std::lock_guard<std::mutex> g(mu);
+        for (const Entry& e : cache)
+            if (e.dev == dev && e.kern == (const void*)kern && e.lds == lds) {
+                *out = e.blocks;
+                return hipSuccess;
+            }
+    }
+    int cus = 0, per_cu = 0;
+    err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (err == hipSuccess) err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, kFusedThreads, lds);
+    if (err != hipSuccess) return err;
+    *out = (long long)per_cu * cus;
+    std::lock_guard<std::mutex> g(mu);
+    if (cache.size() < 256) cache.push_back(Entry{dev, (const void*)kern, lds, *out});
+    return hipSuccess;
+}
+
 struct FusedLaunch {
     const FusedArgs& a;
     hipStream_t s;
@@ -245,15 +283,12 @@ struct FusedLaunch {
     hipError_t run() {
         const auto kern = fused_decode_kernel<EPL, LPG>;
         const size_t lds = fused_lds_bytes(a.r.T, a.r.E, a.r.k, a.R);
-        int dev = 0, cus = 0, per_cu = 0;
-        hipError_t err = hipGetDevice(&dev);
-        if (err == hipSuccess) err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-        if (err == hipSuccess)
-            err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, kFusedThreads, lds);
+        long long fits = 0;
+        const hipError_t err = resident_blocks(kern, lds, &fits);
         if (err != hipSuccess) return err;
         // at most half of what the GPU can hold at once: every block must be
         // resident for the barrier, with margin for anything else running
-        const long long resident = (long long)per_cu * cus / 2;
+        const long long resident = fits / 2;
         if (resident < 1) return hipErrorInvalidConfiguration;
         const long long items = (long long)a.r.T * a.units;
         long long want = (items + kFusedWaves - 1) / kFusedWaves;
