@@ -111,9 +111,16 @@ def _check(status: int):
         raise MoeError(status, f"{L.moe_status_string(status).decode()}: {L.moe_last_error().decode()}")
 
 
+_torch_mod = None
+
+
 def _torch():
-    import torch
-    return torch
+    """torch, imported on first use (the module imports without it) and then kept."""
+    global _torch_mod
+    if _torch_mod is None:
+        import torch
+        _torch_mod = torch
+    return _torch_mod
 
 
 def _ptr(t) -> Optional[int]:
@@ -149,7 +156,7 @@ def _need(t, name, dtype, shape=None, device=None):
         raise ValueError(f"{name} is on {t.device}, expected {device}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
-    if shape is not None and tuple(t.shape) != tuple(shape):
+    if shape is not None and t.shape != tuple(shape):
         raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
 
 
