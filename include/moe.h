@@ -17,7 +17,8 @@
  *   - All array pointers are DEVICE pointers owned by the caller; arrays are
  *     dense and row-major.  bf16 values are passed as uint16_t bit patterns.
  *   - The library never allocates or frees memory in these calls and keeps no
- *     state between them.
+ *     data between them; it only remembers per-device facts it looked up once
+ *     (occupancy figures, the address of moe_get_layout_noalloc's table).
  *   - Every call is asynchronous: it validates its arguments on the host,
  *     enqueues kernels on `stream` (a hipStream_t; NULL = the null stream)
  *     and returns without synchronising.
