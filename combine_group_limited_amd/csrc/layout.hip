@@ -374,59 +374,59 @@ __global__ __launch_bounds__(NT) void layout_expert_kernel(LayoutArgs a) {
     // against 7.8 us for the two copies (6.7 us with no check at all; the
     // check in a second walk of its own, 10.3 us).
     const auto walk = [&](auto check_tag) {
-    constexpr bool CHECK = decltype(check_tag)::value;
-    for (int it0 = 0; it0 < iters; it0 += kExpertLayoutBatch) {
-        TokenRow<KT> rows[kExpertLayoutBatch];
+        constexpr bool CHECK = decltype(check_tag)::value;
+        for (int it0 = 0; it0 < iters; it0 += kExpertLayoutBatch) {
+            TokenRow<KT> rows[kExpertLayoutBatch];
 #pragma unroll
-        for (int b = 0; b < kExpertLayoutBatch; ++b) {
-            const int t = (it0 + b) * NT + tid;
-            if (KT > 0 && it0 + b < iters && t < T) rows[b].load(a.idx + (size_t)t * k);
-        }
-#pragma unroll
-        for (int b = 0; b < kExpertLayoutBatch; ++b) {
-            const int it = it0 + b;
-            if (it >= iters) break;  // block-uniform
-            const int t = it * NT + tid;
-            int js = -1;
-            if (t < T) {
-                bool hit_rank = false;
-                // slots in descending order, so js ends as the first slot
-                // holding e (a repeated index is flagged by expert 0's block)
-                for (int j = (KT > 0 ? KT : k) - 1; j >= 0; --j) {
-                    const unsigned ej = (unsigned)(KT > 0 ? rows[b].e[j] : a.idx[(size_t)t * k + j]);
-                    lt += ej < (unsigned)e ? 1 : 0;
-                    js = ej == (unsigned)e ? j : js;
-                    hit_rank |= ej - r0 < (unsigned)Er;
-                }
-                rk += (rank_block && hit_rank) ? 1 : 0;
-                if constexpr (CHECK) {
-                    // every pair: an index outside [0, E) or repeated in the
-                    // token raises the flag (branch-free; the pairs' pos -1
-                    // is written only in waves that saw one); padded, the
-                    // counts of every expert for the overflow flag
-                    const auto bad_pair = [&](int j) {
-                        const int ej = KT > 0 ? rows[b].e[j] : a.idx[(size_t)t * k + j];
-                        bool dup = false;
-                        for (int i = 0; i < j; ++i) dup |= (KT > 0 ? rows[b].e[i] : a.idx[(size_t)t * k + i]) == ej;
-                        return (unsigned)ej >= (unsigned)a.E || dup;
-                    };
-                    bool tbad = false;
-                    for (int j = 0; j < (KT > 0 ? KT : k); ++j) tbad |= bad_pair(j);
-                    bad |= tbad ? 1 : 0;
-                    if (__ballot(tbad)) {  // rare
-                        for (int j = 0; j < (KT > 0 ? KT : k); ++j)
-                            if (tbad && bad_pair(j)) a.pos[(size_t)t * k + j] = -1;
-                    }
-                    if (count_all)
-                        for (int j = 0; j < (KT > 0 ? KT : k); ++j)
-                            if (!bad_pair(j)) atomicAdd(&hist[KT > 0 ? rows[b].e[j] : a.idx[(size_t)t * k + j]], 1);
-                }
+            for (int b = 0; b < kExpertLayoutBatch; ++b) {
+                const int t = (it0 + b) * NT + tid;
+                if (KT > 0 && it0 + b < iters && t < T) rows[b].load(a.idx + (size_t)t * k);
             }
-            slot[it * NT + tid] = (int8_t)js;
-            const uint64_t bal = __ballot(js >= 0);
-            if (lane == 0) ballots[it * kWaves + w] = bal;
+#pragma unroll
+            for (int b = 0; b < kExpertLayoutBatch; ++b) {
+                const int it = it0 + b;
+                if (it >= iters) break;  // block-uniform
+                const int t = it * NT + tid;
+                int js = -1;
+                if (t < T) {
+                    bool hit_rank = false;
+                    // slots in descending order, so js ends as the first slot
+                    // holding e (a repeated index is flagged by expert 0's block)
+                    for (int j = (KT > 0 ? KT : k) - 1; j >= 0; --j) {
+                        const unsigned ej = (unsigned)(KT > 0 ? rows[b].e[j] : a.idx[(size_t)t * k + j]);
+                        lt += ej < (unsigned)e ? 1 : 0;
+                        js = ej == (unsigned)e ? j : js;
+                        hit_rank |= ej - r0 < (unsigned)Er;
+                    }
+                    rk += (rank_block && hit_rank) ? 1 : 0;
+                    if constexpr (CHECK) {
+                        // every pair: an index outside [0, E) or repeated in the
+                        // token raises the flag (branch-free; the pairs' pos -1
+                        // is written only in waves that saw one); padded, the
+                        // counts of every expert for the overflow flag
+                        const auto bad_pair = [&](int j) {
+                            const int ej = KT > 0 ? rows[b].e[j] : a.idx[(size_t)t * k + j];
+                            bool dup = false;
+                            for (int i = 0; i < j; ++i) dup |= (KT > 0 ? rows[b].e[i] : a.idx[(size_t)t * k + i]) == ej;
+                            return (unsigned)ej >= (unsigned)a.E || dup;
+                        };
+                        bool tbad = false;
+                        for (int j = 0; j < (KT > 0 ? KT : k); ++j) tbad |= bad_pair(j);
+                        bad |= tbad ? 1 : 0;
+                        if (__ballot(tbad)) {  // rare
+                            for (int j = 0; j < (KT > 0 ? KT : k); ++j)
+                                if (tbad && bad_pair(j)) a.pos[(size_t)t * k + j] = -1;
+                        }
+                        if (count_all)
+                            for (int j = 0; j < (KT > 0 ? KT : k); ++j)
+                                if (!bad_pair(j)) atomicAdd(&hist[KT > 0 ? rows[b].e[j] : a.idx[(size_t)t * k + j]], 1);
+                    }
+                }
+                slot[it * NT + tid] = (int8_t)js;
+                const uint64_t bal = __ballot(js >= 0);
+                if (lane == 0) ballots[it * kWaves + w] = bal;
+            }
         }
-    }
     };
     if (check)
         walk(std::true_type{});
