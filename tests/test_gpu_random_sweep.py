@@ -1,4 +1,4 @@
-"""A seeded random sweep of the whole path through the C ABI against the oracle.
+"""Seeded random sweeps through the C ABI against the oracle.
 
 Each case draws one configuration from the shapes the API accepts -- E up to
 512 with any group count dividing it, k up to 16, a rank count dividing E,
@@ -8,7 +8,9 @@ tie-heavy logits, T from 0 to 1500 -- and runs route -> layout -> dispatch ->
 combine on the GPU.  Every stage is checked against the oracle on the GPU's
 own inputs to that stage: indices and weights, every layout array and the
 flags, FP8 codes and scales (or BF16 copies, untouched rows included) bit for
-bit, the combine within its bound (tests/bounds.py)."""
+bit, the combine within its bound (tests/bounds.py).  The same generator
+also draws configurations for the one-launch route + layout + dispatch
+(at most 1024 tokens, within its LDS limit) and for the backward pair."""
 import sys
 
 import numpy as np
@@ -129,3 +131,97 @@ def test_random_configuration(case):
         return
     bad, rel, _ = bounds.combine_check(bf16_from_dev(out), ref, y, rlay["pos"], rw)
     assert bad == 0, f"{bad} combine outputs outside the bound (max rel {rel:.3g})"
+
+
+def fused_lds_bytes(T, E, k, R):
+    """The one-launch decode path's LDS need, as include/moe.h states it."""
+    return 8 * ((T + 63) // 64) * (E + R) + 4 * (2 * E + 1 + T * k + 2048)
+
+
+@pytest.mark.parametrize("case", range(20))
+def test_random_route_dispatch(case):
+    """The one-launch route + layout + dispatch on drawn configurations of at
+    most 1024 tokens: every output bit for bit against the oracle."""
+    c = draw(500 + case)
+    T = min(c["T"], 1024)
+    E, G, g, k, R, H, C, A = (c[n] for n in ("E", "G", "g", "k", "R", "H", "C", "A"))
+    if fused_lds_bytes(T, E, k, R) > 64512:
+        pytest.skip("beyond the one-launch LDS limit")
+    say(f"[gpu] random route_dispatch case {case}: {dict(c, T=T)}")
+    rng = np.random.default_rng(c["seed"])
+    logits = rng.standard_normal((T, E), dtype=np.float32)
+    if c["ties"]:
+        logits = W.tie_heavy(logits)
+    sf = oracle.SOFTMAX if c["score"] == "softmax" else oracle.SIGMOID
+    x = W.f32_to_bf16_bits(rng.standard_normal((T, H), dtype=np.float32))
+    ridx, rw = oracle.route(logits, G, g, k, score_fn=sf, renormalize=c["renorm"], group_topn=c["topn"])
+    rlay = oracle.layout(ridx, E, R, C, A)
+    N = moe.recv_rows(T, E, k, C, A)
+    fp8 = c["dtype"] != "bf16"
+    S = H // 128
+    if fp8:
+        rrx = np.full((N, H), 0xA5, np.uint8)
+        rrs = np.full((N, S), 0xEE, np.uint8) if c["dtype"] == "fp8_ue8m0" else np.full((N, S), -3.0, np.float32)
+        rx, rs = torch.from_numpy(rrx.copy()).to(DEV), torch.from_numpy(rrs.copy()).to(DEV)
+    else:
+        rrx, rrs = np.full((N, H), 0x7A5A, np.uint16), None
+        rx, rs = bf16_to_dev(rrx.copy()), None
+    rrx, rrs = oracle.dispatch(x, rlay["pos"], N, ODT[c["dtype"]], rrx, rrs)
+    lay = moe.alloc_layout(T, E, k, R, C, DEV, A)[0]
+    idx = torch.full((T, k), -5, dtype=torch.int32, device=DEV)
+    w = torch.full((T, k), -5.0, dtype=torch.float32, device=DEV)
+    idx, w, lay, rx, rs = moe.route_dispatch(torch.from_numpy(logits).to(DEV), bf16_to_dev(x), G, g, k, R, C,
+                                             c["dtype"], c["score"], c["renorm"], c["topn"], A,
+                                             out=(idx, w, lay, rx, rs))
+    torch.cuda.synchronize()
+    assert np.array_equal(idx.cpu().numpy(), ridx), "idx"
+    assert np.array_equal(w.cpu().numpy().view(np.uint32), rw.view(np.uint32)), "w"
+    for name in ("cnt_e", "cnt_r", "off_e", "off_r", "pos", "recv_src"):
+        assert np.array_equal(getattr(lay, name).cpu().numpy(), rlay[name]), name
+    assert int(lay.flags.item()) == rlay["flags"], "flags"
+    if fp8:
+        assert np.array_equal(rx.cpu().numpy(), rrx), "recv_x"
+        assert np.array_equal(rs.cpu().numpy().view(np.uint8), rrs.view(np.uint8)), "recv_scales"
+    else:
+        assert np.array_equal(bf16_from_dev(rx), rrx), "recv_x"
+
+
+@pytest.mark.parametrize("case", range(20))
+def test_random_backward(case):
+    """combine_backward (grad_y bit for bit, grad_w within 1e-5 of the
+    products' magnitude) and dispatch_backward (the combine bound with unit
+    weights) on drawn configurations."""
+    c = draw(800 + case)
+    T, E, G, g, k, R, C, A = (c[n] for n in ("T", "E", "G", "g", "k", "R", "C", "A"))
+    H = c["H"] if c["H"] % 8 == 0 else 8
+    say(f"[gpu] random backward case {case}: {dict(c, H=H)}")
+    rng = np.random.default_rng(c["seed"])
+    logits = rng.standard_normal((T, E), dtype=np.float32)
+    sf = oracle.SOFTMAX if c["score"] == "softmax" else oracle.SIGMOID
+    ridx, rw = oracle.route(logits, G, g, k, score_fn=sf, renormalize=c["renorm"], group_topn=c["topn"])
+    pos = oracle.layout(ridx, E, R, C, A)["pos"]
+    N = moe.recv_rows(T, E, k, C, A)
+    gout = W.f32_to_bf16_bits(rng.standard_normal((T, H), dtype=np.float32))
+    y = W.f32_to_bf16_bits(rng.standard_normal((max(N, 1), H), dtype=np.float32))[:N]
+    fill = np.full((N, H), 0x7FC1, np.uint16)
+    ref_gy, ref_gw = oracle.combine_backward(gout, y, pos, rw, grad_y=fill.copy())
+    gy, gw = moe.combine_backward(bf16_to_dev(gout), bf16_to_dev(y), torch.from_numpy(pos).to(DEV),
+                                  torch.from_numpy(rw).to(DEV), grad_y=bf16_to_dev(fill.copy()))
+    gx = moe.dispatch_backward(bf16_to_dev(y), torch.from_numpy(pos).to(DEV))
+    torch.cuda.synchronize()
+    assert np.array_equal(bf16_from_dev(gy), ref_gy), "grad_y"
+    if T == 0:
+        return
+    gwh = gw.cpu().numpy().astype(np.float64)
+    gf = W.bf16_bits_to_f32(gout).astype(np.float64)
+    yf = W.bf16_bits_to_f32(y).astype(np.float64)
+    mag = np.zeros(pos.shape)
+    for j in range(k):
+        ok = pos[:, j] >= 0
+        mag[ok, j] = np.abs(gf[ok] * yf[pos[ok, j]]).sum(1)
+    err = np.abs(gwh - ref_gw.astype(np.float64))
+    assert np.all(err <= 1e-5 * mag + 1e-30), "grad_w"
+    assert np.all(gwh[pos < 0] == 0), "grad_w of dropped pairs"
+    ref_gx = oracle.dispatch_backward(y, pos)
+    bad, rel, _ = bounds.combine_check(bf16_from_dev(gx), ref_gx, y, pos, np.ones((T, k), np.float32))
+    assert bad == 0, f"{bad} grad_x outside the bound (max rel {rel:.3g})"
