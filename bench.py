@@ -450,7 +450,7 @@ def mlp_main(args, torch, moe, hev, dev):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): this build has no "
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the library has no "
               "inter-GPU transport; run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 

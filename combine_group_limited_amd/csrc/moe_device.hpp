@@ -66,7 +66,7 @@ __device__ __forceinline__ float exp_fixed(float z) {
 
 __device__ __forceinline__ float sigmoid_fixed(float x) {
     const float e = exp_fixed(-x);
-    return 1.0f / (1.0f + e);  // IEEE division (no fast-math in this build)
+    return 1.0f / (1.0f + e);  // IEEE division (the library is compiled without fast-math)
 }
 
 // ---------------------------------------------------------------------------

@@ -49,7 +49,7 @@ typedef enum {
     MOE_OK = 0,
     MOE_ERR_INVALID = 1,     /* bad shape, null pointer, or inconsistent sizes */
     MOE_ERR_WORKSPACE = 2,   /* workspace missing or smaller than required */
-    MOE_ERR_UNSUPPORTED = 4, /* valid request this build does not implement */
+    MOE_ERR_UNSUPPORTED = 4, /* valid request the library does not implement */
     MOE_ERR_HIP = 5          /* a HIP runtime call or kernel launch failed */
 } moe_status;
 
